@@ -1,0 +1,213 @@
+/*
+ * CPU oracle for the grouped-int4 (fmt=4, gs=64) MoE expert path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * Plain, slow, obviously correct: scalar loops, every weight decoded on the
+ * spot, all arithmetic in double.  Inputs arrive as given (f32 scales, and
+ * activations already widened exactly to double by the caller).
+ *
+ * Sources (pages, by title and section):
+ *  - colibri pull request "cuda+engine: full fmt=4 (grouped int4 gs=64)
+ *    support + diagnostic harness":
+ *      * Summary / Problem: one f32 scale per 64 consecutive input elements
+ *        of a row instead of one per row; int4 rows are (I+1)/2 bytes, the
+ *        same packed layout as the per-row int4 format.
+ *      * comment "implementation complete but system-instability": the
+ *        on-disk container stores unsigned offset nibbles 0..15 and the GPU
+ *        upload turns them into two's complement with a byte XOR of 0x88.
+ *      * comment "blocked by GPU driver instability": the scale of element
+ *        (o, i) is scales[o*ng + i/gs] with ng = ceil(I/gs); the CPU kernel
+ *        accumulates per group and applies that group's scale; the fused
+ *        gate+up pair reads x once for both matrices.
+ *      * maintainer comment "Here's the oracle you're missing": the
+ *        reference is a plain dequant in double; the fused pair must equal
+ *        two single passes element by element.
+ *  - pxq_llama.cpp release notes, section "Device-side MoE row map": the
+ *    token-to-expert table (histogram, scan, fill) for one batched MoE
+ *    layer.
+ *
+ * Readings taken where the pages are silent (each listed with its reason in
+ * the design notes of this repository):
+ *  - nibble order: element 2j in the LOW nibble of byte j, 2j+1 in the high
+ *    nibble; a pad nibble for odd I holds 8 (value 0);
+ *  - nibble value u stores q = u - 8 (offset binary);
+ *  - SiLU(z) = z / (1 + exp(-z)); expert FFN = down(silu(gate x) * (up x));
+ *  - layer output = sum over the k routing slots, in slot order, of
+ *    weight * expert_ffn(x); ids outside [0, E) are dropped and counted;
+ *  - worklist = stable counting sort of pair p = t*K + k by expert id.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- format sizes (pull request: Summary, "row_bytes"; scale count O*ng) */
+
+int64_t orc_row_bytes(int64_t cols) { return (cols + 1) / 2; }
+
+int64_t orc_groups(int64_t cols, int64_t gs) { return (cols + gs - 1) / gs; }
+
+int64_t orc_packed_bytes(int64_t rows, int64_t cols) {
+    return rows * orc_row_bytes(cols);
+}
+
+int64_t orc_scale_count(int64_t rows, int64_t cols, int64_t gs) {
+    return rows * orc_groups(cols, gs);
+}
+
+/* ---- pack / unpack (offset-binary nibbles, low nibble = even element) -- */
+
+/* Returns the number of codes outside [-8, 7]; those are stored wrapped. */
+int64_t orc_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed) {
+    int64_t bad = 0;
+    int64_t rb = orc_row_bytes(cols);
+    for (int64_t o = 0; o < rows; o++) {
+        for (int64_t j = 0; j < rb; j++) {
+            int lo_u = 8, hi_u = 8;            /* pad nibble = value 0 */
+            int64_t i0 = 2 * j, i1 = 2 * j + 1;
+            int v0 = q[o * cols + i0];
+            if (v0 < -8 || v0 > 7) bad++;
+            lo_u = (v0 + 8) & 15;
+            if (i1 < cols) {
+                int v1 = q[o * cols + i1];
+                if (v1 < -8 || v1 > 7) bad++;
+                hi_u = (v1 + 8) & 15;
+            }
+            packed[o * rb + j] = (uint8_t)(lo_u | (hi_u << 4));
+        }
+    }
+    return bad;
+}
+
+/* The signed code of element (o, i): nibble value minus 8. */
+int orc_code(const uint8_t *packed, int64_t cols, int64_t o, int64_t i) {
+    uint8_t byte = packed[o * orc_row_bytes(cols) + i / 2];
+    int u = (i % 2 == 0) ? (byte & 15) : (byte >> 4);
+    return u - 8;
+}
+
+void orc_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q) {
+    for (int64_t o = 0; o < rows; o++)
+        for (int64_t i = 0; i < cols; i++)
+            q[o * cols + i] = (int8_t)orc_code(packed, cols, o, i);
+}
+
+/* Dequantised weight: scales[o*ng + i/gs] * code. */
+double orc_weight(const uint8_t *packed, const float *scales, int64_t cols,
+                  int64_t gs, int64_t o, int64_t i) {
+    int64_t ng = orc_groups(cols, gs);
+    double s = (double)scales[o * ng + i / gs];
+    return s * (double)orc_code(packed, cols, o, i);
+}
+
+/* ---- matvec: y[b, o] = sum_i deq(W)[o, i] * x[b, i] -------------------- */
+
+void orc_matvec(const uint8_t *packed, const float *scales, int64_t rows,
+                int64_t cols, int64_t gs, const double *x, int64_t batch,
+                double *y) {
+    for (int64_t b = 0; b < batch; b++)
+        for (int64_t o = 0; o < rows; o++) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < cols; i++)
+                acc += orc_weight(packed, scales, cols, gs, o, i) *
+                       x[b * cols + i];
+            y[b * rows + o] = acc;
+        }
+}
+
+/* Fused gate+up pair: by definition the two single matvecs. */
+void orc_pair(const uint8_t *pg, const float *sg, const uint8_t *pu,
+              const float *su, int64_t rows, int64_t cols, int64_t gs,
+              const double *x, int64_t batch, double *yg, double *yu) {
+    orc_matvec(pg, sg, rows, cols, gs, x, batch, yg);
+    orc_matvec(pu, su, rows, cols, gs, x, batch, yu);
+}
+
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One expert: out = down(silu(gate x) * (up x)).
+ * gate/up are [inter x hidden], down is [hidden x inter]. */
+void orc_ffn(const uint8_t *pg, const float *sg, const uint8_t *pu,
+             const float *su, const uint8_t *pd, const float *sd,
+             int64_t hidden, int64_t inter, int64_t gs, const double *x,
+             int64_t batch, double *out) {
+    double *g = (double *)malloc(sizeof(double) * (size_t)inter);
+    double *u = (double *)malloc(sizeof(double) * (size_t)inter);
+    double *h = (double *)malloc(sizeof(double) * (size_t)inter);
+    for (int64_t b = 0; b < batch; b++) {
+        const double *xb = x + b * hidden;
+        orc_pair(pg, sg, pu, su, inter, hidden, gs, xb, 1, g, u);
+        for (int64_t f = 0; f < inter; f++) h[f] = orc_silu(g[f]) * u[f];
+        orc_matvec(pd, sd, hidden, inter, gs, h, 1, out + b * hidden);
+    }
+    free(g);
+    free(u);
+    free(h);
+}
+
+/* ---- worklist: stable counting sort of pairs by expert ------------------
+ * pairs[0..n_valid) hold pair ids p = t*K + k grouped by expert in
+ * ascending expert order and ascending p inside one expert; pairs[n_valid..)
+ * and inv[] of dropped pairs are -1.  offsets[E] = n_valid.  Returns the
+ * number of dropped ids (outside [0, E)). */
+int64_t orc_worklist(const int32_t *ids, int64_t tokens, int64_t k,
+                     int64_t experts, int32_t *counts, int32_t *offsets,
+                     int32_t *pairs, int32_t *inv) {
+    int64_t n = tokens * k, bad = 0;
+    for (int64_t e = 0; e < experts; e++) counts[e] = 0;
+    for (int64_t p = 0; p < n; p++) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= experts) bad++;
+        else counts[e]++;
+    }
+    offsets[0] = 0;
+    for (int64_t e = 0; e < experts; e++) offsets[e + 1] = offsets[e] + counts[e];
+    for (int64_t p = 0; p < n; p++) { pairs[p] = -1; inv[p] = -1; }
+    int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)(experts + 1));
+    for (int64_t e = 0; e < experts; e++) fill[e] = offsets[e];
+    for (int64_t p = 0; p < n; p++) {
+        int32_t e = ids[p];
+        if (e < 0 || e >= experts) continue;
+        pairs[fill[e]] = (int32_t)p;
+        inv[p] = fill[e];
+        fill[e]++;
+    }
+    free(fill);
+    return bad;
+}
+
+/* ---- layer: out[t] = sum_k w[t,k] * ffn_{ids[t,k]}(x_t) -----------------
+ * Weights are stacked per expert: gate/up codes at pg + e*stride_gu_q with
+ * scales at sg + e*stride_gu_s, down at pd + e*stride_d_q / sd + ... */
+int64_t orc_layer(const uint8_t *pg, const float *sg, const uint8_t *pu,
+                  const float *su, const uint8_t *pd, const float *sd,
+                  int64_t experts, int64_t hidden, int64_t inter, int64_t gs,
+                  const double *x, int64_t tokens, const int32_t *ids,
+                  const float *w, int64_t k, double *out) {
+    int64_t gu_q = orc_packed_bytes(inter, hidden);
+    int64_t gu_s = orc_scale_count(inter, hidden, gs);
+    int64_t d_q = orc_packed_bytes(hidden, inter);
+    int64_t d_s = orc_scale_count(hidden, inter, gs);
+    int64_t bad = 0;
+    double *y = (double *)malloc(sizeof(double) * (size_t)hidden);
+    for (int64_t t = 0; t < tokens; t++) {
+        double *ot = out + t * hidden;
+        for (int64_t j = 0; j < hidden; j++) ot[j] = 0.0;
+        for (int64_t s = 0; s < k; s++) {
+            int32_t e = ids[t * k + s];
+            if (e < 0 || e >= experts) { bad++; continue; }
+            orc_ffn(pg + e * gu_q, sg + e * gu_s, pu + e * gu_q, su + e * gu_s,
+                    pd + e * d_q, sd + e * d_s, hidden, inter, gs,
+                    x + t * hidden, 1, y);
+            double wt = (double)w[t * k + s];
+            for (int64_t j = 0; j < hidden; j++) ot[j] += wt * y[j];
+        }
+    }
+    free(y);
+    return bad;
+}
