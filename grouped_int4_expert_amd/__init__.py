@@ -1,0 +1,335 @@
+"""Python binding of libqmoe.so (grouped int4, gs = 64, MoE expert matmul on
+MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qmoe.h``.  PyTorch provides
+device memory and the current stream.  There is no CPU fallback: if the
+library is missing or a call fails, an exception is raised.
+
+Names mirror the C entry points (``qmoe_pack``, ``qmoe_matvec``,
+``qmoe_expert_ffn``, ``qmoe_worklist``, ``qmoe_layer`` ...).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+ABI_VERSION = 1
+
+QMOE_OK = 0
+QMOE_F32 = 0
+QMOE_BF16 = 1
+STATUS = {0: "QMOE_OK", 1: "QMOE_ERR_NULL", 2: "QMOE_ERR_SHAPE", 3: "QMOE_ERR_ALIGN",
+          4: "QMOE_ERR_UNSUPPORTED", 5: "QMOE_ERR_WORKSPACE", 6: "QMOE_ERR_ALIAS",
+          7: "QMOE_ERR_ABI", 8: "QMOE_ERR_HIP"}
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib_status_str(status)})")
+
+
+class qmoe_qmat(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("rows", ctypes.c_int32),
+                ("cols", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("s", ctypes.c_void_p),
+                ("q_expert_stride", ctypes.c_int64), ("s_expert_stride", ctypes.c_int64)]
+
+
+class qmoe_layer_desc(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("experts", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("gate", qmoe_qmat), ("up", qmoe_qmat),
+                ("down", qmoe_qmat)]
+
+
+class qmoe_layer_ws_view(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("counts", ctypes.c_int64),
+                ("offsets", ctypes.c_int64), ("pairs", ctypes.c_int64),
+                ("inv", ctypes.c_int64), ("n_invalid", ctypes.c_int64)]
+
+
+EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_scale_count",
+           "qmoe_pack", "qmoe_unpack", "qmoe_matvec_workspace_bytes", "qmoe_matvec",
+           "qmoe_expert_ffn_workspace_bytes", "qmoe_expert_ffn",
+           "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
+           "qmoe_layer", "qmoe_layer_ws_layout"]
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libqmoe.so and declare signatures.  Raises if it is missing or
+    was built from another ABI version."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"libqmoe.so not built ({p}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "qmoe_abi_version": (ctypes.c_int, []),
+        "qmoe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "qmoe_packed_bytes": (sz, [i64, i64]),
+        "qmoe_scale_count": (sz, [i64, i64, i64]),
+        "qmoe_pack": (ctypes.c_int, [vp, i64, i64, vp, vp, vp]),
+        "qmoe_unpack": (ctypes.c_int, [vp, i64, i64, vp, vp]),
+        "qmoe_matvec_workspace_bytes": (sz, [ctypes.POINTER(qmoe_qmat), i32]),
+        "qmoe_matvec": (ctypes.c_int, [ctypes.POINTER(qmoe_qmat), vp, i32, vp, vp, sz, vp]),
+        "qmoe_expert_ffn_workspace_bytes": (sz, [ctypes.POINTER(qmoe_qmat)] * 3 + [i32, i32]),
+        "qmoe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(qmoe_qmat)] * 3 +
+                            [i32, vp, i32, vp, vp, sz, vp]),
+        "qmoe_worklist_workspace_bytes": (sz, [i32, i32, i32]),
+        "qmoe_worklist": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "qmoe_layer_workspace_bytes": (sz, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32]),
+        "qmoe_layer": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, vp,
+                                      i32, vp, vp, sz, vp]),
+        "qmoe_layer_ws_layout": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32,
+                                                ctypes.POINTER(qmoe_layer_ws_view)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    v = lib.qmoe_abi_version()
+    if v != ABI_VERSION:
+        raise ImportError(f"libqmoe.so ABI {v}, binding expects {ABI_VERSION}")
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _lib_status_str(status):
+    try:
+        return load().qmoe_status_str(int(status)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def _check(status, what):
+    if status != QMOE_OK:
+        raise QmoeError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+# ------------------------------------------------------------------ sizes ---
+
+def qmoe_abi_version() -> int:
+    return int(load().qmoe_abi_version())
+
+
+def qmoe_status_str(status: int) -> str:
+    return load().qmoe_status_str(int(status)).decode()
+
+
+def qmoe_packed_bytes(rows: int, cols: int) -> int:
+    return int(load().qmoe_packed_bytes(rows, cols))
+
+
+def qmoe_scale_count(rows: int, cols: int, group: int = 64) -> int:
+    return int(load().qmoe_scale_count(rows, cols, group))
+
+
+# ----------------------------------------------------------------- format ---
+
+def qmoe_pack(q: torch.Tensor, out: torch.Tensor | None = None, count_bad: bool = False,
+              stream=None):
+    """int8 codes [..., rows, cols] -> packed uint8 [..., rows, ceil(cols/2)].
+    Returns packed (and the device count of out-of-range codes if asked)."""
+    _dev(q, "q", torch.int8)
+    cols = q.shape[-1]
+    rows = q.numel() // cols if cols else 0
+    if out is None:
+        out = torch.empty(*q.shape[:-1], (cols + 1) // 2, dtype=torch.uint8, device=q.device)
+    nbad = torch.empty(4, dtype=torch.int32, device=q.device) if count_bad else None
+    _check(load().qmoe_pack(_ptr(q), rows, cols, _ptr(out), _ptr(nbad), _stream(stream)),
+           "qmoe_pack")
+    return (out, nbad[:1]) if count_bad else out
+
+
+def qmoe_unpack(packed: torch.Tensor, cols: int, stream=None):
+    _dev(packed, "packed", torch.uint8)
+    rows = packed.numel() // packed.shape[-1] if packed.numel() else 0
+    out = torch.empty(*packed.shape[:-1], cols, dtype=torch.int8, device=packed.device)
+    _check(load().qmoe_unpack(_ptr(packed), rows, cols, _ptr(out), _stream(stream)),
+           "qmoe_unpack")
+    return out
+
+
+# ------------------------------------------------------------ descriptors ---
+
+def make_qmat(q: torch.Tensor, s: torch.Tensor, cols: int, group: int = 64) -> qmoe_qmat:
+    """Descriptor of packed codes q [E?, rows, cols/2] and scales s [E?, rows, ng]."""
+    rows = q.shape[-2]
+    m = qmoe_qmat()
+    m.struct_size = ctypes.sizeof(qmoe_qmat)
+    m.rows, m.cols, m.group = rows, cols, group
+    m.q = q.data_ptr()
+    m.s = s.data_ptr()
+    m.q_expert_stride = q.stride(0) if q.dim() == 3 else 0
+    m.s_expert_stride = s.stride(0) if s.dim() == 3 else 0
+    return m
+
+
+class QLayer:
+    """Stacked int4-g64 weights of one MoE layer resident on the device.
+
+    gate/up packed [E, F, H/2] + scales [E, F, H/64]; down packed [E, H, F/2]
+    + scales [E, H, F/64]."""
+
+    def __init__(self, pg, sg, pu, su, pd, sd, hidden, inter, group=64):
+        self.tensors = [pg, sg, pu, su, pd, sd]
+        for t, n in zip(self.tensors, ("pg", "sg", "pu", "su", "pd", "sd")):
+            _dev(t, n)
+        self.experts = pg.shape[0]
+        self.hidden, self.inter, self.group = hidden, inter, group
+        d = qmoe_layer_desc()
+        d.struct_size = ctypes.sizeof(qmoe_layer_desc)
+        d.experts, d.hidden, d.inter, d.group = self.experts, hidden, inter, group
+        d.gate = make_qmat(pg, sg, hidden, group)
+        d.up = make_qmat(pu, su, hidden, group)
+        d.down = make_qmat(pd, sd, inter, group)
+        self.desc = d
+
+    def workspace_bytes(self, tokens, k, x_dtype):
+        return int(load().qmoe_layer_workspace_bytes(ctypes.byref(self.desc), tokens, k,
+                                                     x_dtype))
+
+    def ws_view(self, tokens, k, x_dtype):
+        v = qmoe_layer_ws_view()
+        v.struct_size = ctypes.sizeof(qmoe_layer_ws_view)
+        _check(load().qmoe_layer_ws_layout(ctypes.byref(self.desc), tokens, k, x_dtype,
+                                           ctypes.byref(v)), "qmoe_layer_ws_layout")
+        return v
+
+
+def _dtype_code(x):
+    if x.dtype == torch.float32:
+        return QMOE_F32
+    if x.dtype == torch.bfloat16:
+        return QMOE_BF16
+    raise TypeError("x must be float32 (decode path) or bfloat16 (prefill path)")
+
+
+def _workspace(nbytes, device, ws):
+    if ws is not None:
+        if ws.numel() < nbytes:
+            raise ValueError(f"workspace of {ws.numel()} bytes < {nbytes}")
+        return ws
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ calls ---
+
+def qmoe_matvec(pq, s, cols, x, group=64, out=None, ws=None, stream=None):
+    """y = W x; W packed [rows, cols/2] + scales [rows, ng]; x f32 [B, cols]."""
+    _dev(x, "x", torch.float32)
+    W = make_qmat(pq, s, cols, group)
+    batch = x.shape[0] if x.dim() == 2 else 1
+    y = out if out is not None else torch.empty(batch, W.rows, dtype=torch.float32,
+                                                device=x.device)
+    nb = int(load().qmoe_matvec_workspace_bytes(ctypes.byref(W), batch))
+    ws = _workspace(nb, x.device, ws)
+    _check(load().qmoe_matvec(ctypes.byref(W), _ptr(x), batch, _ptr(y), _ptr(ws), ws.numel(),
+                              _stream(stream)), "qmoe_matvec")
+    return y
+
+
+def qmoe_expert_ffn(pg, sg, pu, su, pd, sd, hidden, inter, x, group=64, out=None, ws=None,
+                    stream=None):
+    """out = down(silu(gate x) * (up x)) for one expert; x f32 or bf16 [B, H]."""
+    _dev(x, "x")
+    code = _dtype_code(x)
+    G = make_qmat(pg, sg, hidden, group)
+    U = make_qmat(pu, su, hidden, group)
+    D = make_qmat(pd, sd, inter, group)
+    batch = x.shape[0]
+    o = out if out is not None else torch.empty(batch, hidden, dtype=torch.float32,
+                                                device=x.device)
+    nb = int(load().qmoe_expert_ffn_workspace_bytes(ctypes.byref(G), ctypes.byref(U),
+                                                    ctypes.byref(D), code, batch))
+    ws = _workspace(nb, x.device, ws)
+    _check(load().qmoe_expert_ffn(ctypes.byref(G), ctypes.byref(U), ctypes.byref(D), code,
+                                  _ptr(x), batch, _ptr(o), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "qmoe_expert_ffn")
+    return o
+
+
+def qmoe_worklist(topk_ids, experts, ws=None, stream=None):
+    """Device worklist for int32 ids [T, k]; returns a dict of device tensors."""
+    _dev(topk_ids, "topk_ids", torch.int32)
+    T, k = topk_ids.shape
+    n = T * k
+    dev = topk_ids.device
+    out = dict(counts=torch.empty(experts, dtype=torch.int32, device=dev),
+               offsets=torch.empty(experts + 1, dtype=torch.int32, device=dev),
+               pairs=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+               inv=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
+               n_invalid=torch.empty(1, dtype=torch.int32, device=dev))
+    nb = int(load().qmoe_worklist_workspace_bytes(T, k, experts))
+    ws = _workspace(nb, dev, ws)
+    _check(load().qmoe_worklist(_ptr(topk_ids), T, k, experts, _ptr(out["counts"]),
+                                _ptr(out["offsets"]), _ptr(out["pairs"]), _ptr(out["inv"]),
+                                _ptr(out["n_invalid"]), _ptr(ws), ws.numel(),
+                                _stream(stream)), "qmoe_worklist")
+    out["pairs"] = out["pairs"][:n]
+    out["inv"] = out["inv"][:n]
+    return out
+
+
+def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=None):
+    """Routed MoE layer: out[t] = sum_j w[t,j] * ffn_{ids[t,j]}(x_t)."""
+    _dev(x, "x")
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    code = _dtype_code(x)
+    T, k = topk_ids.shape
+    o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
+                                                device=x.device)
+    nb = layer.workspace_bytes(T, k, code)
+    ws = _workspace(nb, x.device, ws)
+    _check(load().qmoe_layer(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
+                             _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
+           "qmoe_layer")
+    return o
+
+
+def layer_worklist_from_ws(layer: QLayer, ws, tokens, k, x_dtype):
+    """Views of the worklist a qmoe_layer call left in its workspace."""
+    v = layer.ws_view(tokens, k, x_dtype)
+    n = tokens * k
+    b = ws
+
+    def i32(off, cnt):
+        return b[off:off + 4 * cnt].view(torch.int32)
+    E = layer.experts
+    return dict(counts=i32(v.counts, E), offsets=i32(v.offsets, E + 1), pairs=i32(v.pairs, n),
+                inv=i32(v.inv, n), n_invalid=i32(v.n_invalid, 1))

@@ -1,0 +1,432 @@
+// C ABI of libqmoe.so: host-side validation, workspace layout and launch
+// sequencing.  Every check runs before the first HIP call, so a rejected
+// call launches nothing (fail closed).
+#include <string.h>
+
+#include "../../include/qmoe.h"
+#include "launch.h"
+
+using namespace qmoe;
+
+namespace qmoe {
+bool gemv_supported(int cols);
+}
+
+namespace {
+
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_TOPK = 64;
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+inline bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+inline int status_of(hipError_t e) { return e == hipSuccess ? QMOE_OK : QMOE_ERR_HIP; }
+
+int64_t packed_bytes(int64_t rows, int64_t cols) { return rows * ((cols + 1) / 2); }
+int64_t scale_count(int64_t rows, int64_t cols, int64_t g) { return rows * ((cols + g - 1) / g); }
+
+// Validate one matrix descriptor for the GPU kernels: expected shape,
+// group 64, cols % 64 == 0, aligned pointers and expert strides.
+int check_qmat(const qmoe_qmat *m, int rows, int cols, int experts) {
+    if (!m) return QMOE_ERR_NULL;
+    if (m->struct_size != sizeof(qmoe_qmat)) return QMOE_ERR_ABI;
+    if (m->rows != rows || m->cols != cols || rows <= 0 || cols <= 0) return QMOE_ERR_SHAPE;
+    if (m->group <= 0) return QMOE_ERR_SHAPE;
+    if (m->group != 64 || cols % 64 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (!m->q || !m->s) return QMOE_ERR_NULL;
+    if (!aligned16(m->q) || !aligned16(m->s)) return QMOE_ERR_ALIGN;
+    if (experts > 1) {
+        if (m->q_expert_stride < packed_bytes(rows, cols) ||
+            m->s_expert_stride < scale_count(rows, cols, 64))
+            return QMOE_ERR_SHAPE;
+        if (m->q_expert_stride % 16 != 0 || m->s_expert_stride % 4 != 0) return QMOE_ERR_ALIGN;
+    }
+    return QMOE_OK;
+}
+
+QMat to_qmat(const qmoe_qmat *m) {
+    QMat q;
+    q.q = m->q;
+    q.s = m->s;
+    q.q_stride = m->q_expert_stride;
+    q.s_stride = m->s_expert_stride;
+    q.rows = m->rows;
+    q.cols = m->cols;
+    return q;
+}
+
+// Workspace carving with 256-byte alignment.
+struct Carver {
+    char *base;
+    int64_t off = 0;
+    explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+    template <typename T>
+    T *take(int64_t count) {
+        T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+        off = align256(off + count * (int64_t)sizeof(T));
+        return p;
+    }
+};
+
+struct LayerWs {
+    Worklist wl;
+    int32_t *hist;
+    XDigits xd, hd;
+    uint16_t *h16;
+    float *y;
+    int64_t bytes;
+    int max_active, max_tiles;
+    qmoe_layer_ws_view view;
+};
+
+LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
+    LayerWs L{};
+    Carver c(ws);
+    const int64_t n = (int64_t)T * k;
+    L.max_active = (int)(n < E ? n : E);
+    L.max_tiles = (int)((n + MFMA_BM - 1) / MFMA_BM + L.max_active);
+    L.wl.counts = c.take<int32_t>(E);
+    L.wl.offsets = c.take<int32_t>(E + 1);
+    L.wl.pairs = c.take<int32_t>(n);
+    L.wl.inv = c.take<int32_t>(n);
+    L.wl.n_invalid = c.take<int32_t>(1);
+    L.wl.active = c.take<int32_t>(E);
+    L.wl.n_active = c.take<int32_t>(1);
+    L.wl.tiles = c.take<int32_t>(2 * (int64_t)L.max_tiles);
+    L.wl.n_tiles = c.take<int32_t>(1);
+    L.wl.tile_m = MFMA_BM;
+    L.hist = c.take<int32_t>(wl_scratch_ints(n, E));
+    if (dtype == QMOE_F32) {
+        L.xd.dig = c.take<uint32_t>((int64_t)T * (H / 32) * 20);
+        L.xd.fac = c.take<float>((int64_t)T * (H / 32));
+        L.hd.dig = c.take<uint32_t>(n * (F / 32) * 20);
+        L.hd.fac = c.take<float>(n * (F / 32));
+    } else {
+        L.h16 = c.take<uint16_t>(n * F);
+        L.y = c.take<float>(n * H);
+    }
+    L.bytes = c.off;
+    // offsets of the worklist arrays (same order as above)
+    int64_t o = 0;
+    L.view.struct_size = sizeof(qmoe_layer_ws_view);
+    L.view.counts = o;
+    o = align256(o + 4 * (int64_t)E);
+    L.view.offsets = o;
+    o = align256(o + 4 * (int64_t)(E + 1));
+    L.view.pairs = o;
+    o = align256(o + 4 * n);
+    L.view.inv = o;
+    o = align256(o + 4 * n);
+    L.view.n_invalid = o;
+    return L;
+}
+
+int check_layer_desc(const qmoe_layer_desc *d) {
+    if (!d) return QMOE_ERR_NULL;
+    if (d->struct_size != sizeof(qmoe_layer_desc)) return QMOE_ERR_ABI;
+    if (d->experts < 1 || d->experts > MAX_EXPERTS || d->hidden <= 0 || d->inter <= 0)
+        return QMOE_ERR_SHAPE;
+    if (d->group <= 0) return QMOE_ERR_SHAPE;
+    if (d->group != 64 || d->hidden % 64 || d->inter % 64) return QMOE_ERR_UNSUPPORTED;
+    int s;
+    if ((s = check_qmat(&d->gate, d->inter, d->hidden, d->experts))) return s;
+    if ((s = check_qmat(&d->up, d->inter, d->hidden, d->experts))) return s;
+    if ((s = check_qmat(&d->down, d->hidden, d->inter, d->experts))) return s;
+    return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmoe_abi_version(void) { return QMOE_ABI_VERSION; }
+
+const char *qmoe_status_str(int status) {
+    switch (status) {
+        case QMOE_OK: return "ok";
+        case QMOE_ERR_NULL: return "null pointer";
+        case QMOE_ERR_SHAPE: return "bad shape or size";
+        case QMOE_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case QMOE_ERR_UNSUPPORTED: return "unsupported by the GPU kernels (group must be 64, cols % 64 == 0)";
+        case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case QMOE_ERR_ALIAS: return "output overlaps an input or the workspace";
+        case QMOE_ERR_ABI: return "struct_size mismatch (library and caller built from different headers)";
+        case QMOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t qmoe_packed_bytes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return 0;
+    return (size_t)packed_bytes(rows, cols);
+}
+
+size_t qmoe_scale_count(int64_t rows, int64_t cols, int64_t group) {
+    if (rows < 0 || cols < 0 || group <= 0) return 0;
+    return (size_t)scale_count(rows, cols, group);
+}
+
+int qmoe_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed, int32_t *n_bad,
+              void *stream) {
+    if (rows < 0 || cols < 0) return QMOE_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return QMOE_OK;
+    if (!q || !packed) return QMOE_ERR_NULL;
+    if (n_bad && !aligned4(n_bad)) return QMOE_ERR_ALIGN;
+    if (overlap(q, rows * cols, packed, packed_bytes(rows, cols))) return QMOE_ERR_ALIAS;
+    if (n_bad && (overlap(n_bad, 4, q, rows * cols) ||
+                  overlap(n_bad, 4, packed, packed_bytes(rows, cols))))
+        return QMOE_ERR_ALIAS;
+    return status_of(launch_pack(q, rows, cols, packed, n_bad, as_stream(stream)));
+}
+
+int qmoe_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q, void *stream) {
+    if (rows < 0 || cols < 0) return QMOE_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return QMOE_OK;
+    if (!q || !packed) return QMOE_ERR_NULL;
+    if (overlap(q, rows * cols, packed, packed_bytes(rows, cols))) return QMOE_ERR_ALIAS;
+    return status_of(launch_unpack(packed, rows, cols, q, as_stream(stream)));
+}
+
+size_t qmoe_matvec_workspace_bytes(const qmoe_qmat *W, int32_t batch) {
+    if (!W || batch < 0 || W->cols <= 0) return 0;
+    Carver c(nullptr);
+    c.take<uint32_t>((int64_t)batch * (W->cols / 32) * 20);
+    c.take<float>((int64_t)batch * (W->cols / 32));
+    return (size_t)c.off;
+}
+
+int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, void *ws,
+                size_t ws_bytes, void *stream) {
+    if (!W) return QMOE_ERR_NULL;
+    if (W->struct_size != sizeof(qmoe_qmat)) return QMOE_ERR_ABI;
+    if (batch < 0 || W->rows <= 0 || W->cols <= 0 || W->group <= 0) return QMOE_ERR_SHAPE;
+    int s = check_qmat(W, W->rows, W->cols, 1);
+    if (s) return s;
+    if (!gemv_supported(W->cols)) return QMOE_ERR_UNSUPPORTED;
+    if (batch == 0) return QMOE_OK;
+    if (!x || !y) return QMOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_ALIGN;
+    const size_t need = qmoe_matvec_workspace_bytes(W, batch);
+    if (!ws || ws_bytes < need) return QMOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QMOE_ERR_ALIGN;
+    const int64_t xb = (int64_t)batch * W->cols * 4, yb = (int64_t)batch * W->rows * 4;
+    if (overlap(y, yb, x, xb) || overlap(y, yb, ws, need) || overlap(x, xb, ws, need) ||
+        overlap(y, yb, W->q, packed_bytes(W->rows, W->cols)) ||
+        overlap(y, yb, W->s, 4 * scale_count(W->rows, W->cols, 64)))
+        return QMOE_ERR_ALIAS;
+    Carver c(ws);
+    XDigits xd;
+    xd.dig = c.take<uint32_t>((int64_t)batch * (W->cols / 32) * 20);
+    xd.fac = c.take<float>((int64_t)batch * (W->cols / 32));
+    const hipStream_t st = as_stream(stream);
+    hipError_t e = launch_xdigits(x, batch, W->cols, xd, st);
+    if (e == hipSuccess) e = launch_gemv_matvec(to_qmat(W), xd, batch, y, st);
+    return status_of(e);
+}
+
+size_t qmoe_expert_ffn_workspace_bytes(const qmoe_qmat *gate, const qmoe_qmat *up,
+                                       const qmoe_qmat *down, int32_t x_dtype, int32_t batch) {
+    (void)up;
+    (void)down;
+    if (!gate || batch < 0) return 0;
+    const int64_t H = gate->cols, F = gate->rows;
+    Carver c(nullptr);
+    if (x_dtype == QMOE_F32) {
+        c.take<uint32_t>(batch * (H / 32) * 20);
+        c.take<float>(batch * (H / 32));
+        c.take<uint32_t>(batch * (F / 32) * 20);
+        c.take<float>(batch * (F / 32));
+    } else {
+        c.take<uint16_t>(batch * F);
+    }
+    return (size_t)c.off;
+}
+
+int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat *down,
+                    int32_t x_dtype, const void *x, int32_t batch, float *out, void *ws,
+                    size_t ws_bytes, void *stream) {
+    if (!gate || !up || !down) return QMOE_ERR_NULL;
+    if (gate->struct_size != sizeof(qmoe_qmat) || up->struct_size != sizeof(qmoe_qmat) ||
+        down->struct_size != sizeof(qmoe_qmat))
+        return QMOE_ERR_ABI;
+    const int H = gate->cols, F = gate->rows;
+    if (H <= 0 || F <= 0 || batch < 0) return QMOE_ERR_SHAPE;
+    int s;
+    if ((s = check_qmat(gate, F, H, 1))) return s;
+    if ((s = check_qmat(up, F, H, 1))) return s;
+    if ((s = check_qmat(down, H, F, 1))) return s;
+    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
+        return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype == QMOE_BF16 && H % 128 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (batch == 0) return QMOE_OK;
+    if (!x || !out) return QMOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out)) return QMOE_ERR_ALIGN;
+    const size_t need = qmoe_expert_ffn_workspace_bytes(gate, up, down, x_dtype, batch);
+    if (!ws || ws_bytes < need) return QMOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QMOE_ERR_ALIGN;
+    const int64_t xb = (int64_t)batch * H * (x_dtype == QMOE_F32 ? 4 : 2);
+    const int64_t ob = (int64_t)batch * H * 4;
+    if (overlap(out, ob, x, xb) || overlap(out, ob, ws, need) || overlap(x, xb, ws, need))
+        return QMOE_ERR_ALIAS;
+    const hipStream_t st = as_stream(stream);
+    Carver c(ws);
+    hipError_t e;
+    if (x_dtype == QMOE_F32) {
+        XDigits xd, hd;
+        xd.dig = c.take<uint32_t>((int64_t)batch * (H / 32) * 20);
+        xd.fac = c.take<float>((int64_t)batch * (H / 32));
+        hd.dig = c.take<uint32_t>((int64_t)batch * (F / 32) * 20);
+        hd.fac = c.take<float>((int64_t)batch * (F / 32));
+        GemvRoute r{};
+        r.wl.pairs = nullptr;
+        r.ntok = batch;
+        r.k = 1;
+        e = launch_xdigits(static_cast<const float *>(x), batch, H, xd, st);
+        if (e == hipSuccess) e = launch_gemv_gateup(to_qmat(gate), to_qmat(up), xd, hd, r, st);
+        if (e == hipSuccess) e = launch_gemv_down(to_qmat(down), hd, out, r, st);
+    } else {
+        uint16_t *h16 = c.take<uint16_t>((int64_t)batch * F);
+        MfmaRoute r{};
+        r.wl.pairs = nullptr;
+        r.ntok = batch;
+        r.k = 1;
+        e = launch_mfma_gateup(to_qmat(gate), to_qmat(up), static_cast<const uint16_t *>(x), h16,
+                               r, st);
+        if (e == hipSuccess) e = launch_mfma_down(to_qmat(down), h16, out, r, st);
+    }
+    return status_of(e);
+}
+
+size_t qmoe_worklist_workspace_bytes(int32_t tokens, int32_t k, int32_t experts) {
+    if (tokens < 0 || k < 1 || experts < 1) return 0;
+    return (size_t)(4 * wl_scratch_ints((int64_t)tokens * k, experts));
+}
+
+int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k, int32_t experts,
+                  int32_t *counts, int32_t *offsets, int32_t *pairs, int32_t *inv,
+                  int32_t *n_invalid, void *ws, size_t ws_bytes, void *stream) {
+    if (tokens < 0 || k < 1 || k > MAX_TOPK || experts < 1 || experts > MAX_EXPERTS)
+        return QMOE_ERR_SHAPE;
+    if ((int64_t)tokens * k > (int64_t)1 << 30) return QMOE_ERR_SHAPE;
+    if (!counts || !offsets || !n_invalid) return QMOE_ERR_NULL;
+    const int64_t n = (int64_t)tokens * k;
+    if (n > 0 && (!topk_ids || !pairs || !inv)) return QMOE_ERR_NULL;
+    const void *ptrs[6] = {topk_ids, counts, offsets, pairs, inv, n_invalid};
+    for (const void *p : ptrs)
+        if (p && !aligned4(p)) return QMOE_ERR_ALIGN;
+    const size_t need = qmoe_worklist_workspace_bytes(tokens, k, experts);
+    if (need > 0 && (!ws || ws_bytes < need)) return QMOE_ERR_WORKSPACE;
+    const void *outs[5] = {counts, offsets, pairs, inv, n_invalid};
+    const int64_t outn[5] = {4 * (int64_t)experts, 4 * (int64_t)(experts + 1), 4 * n, 4 * n, 4};
+    for (int i = 0; i < 5; i++) {
+        if (overlap(outs[i], outn[i], topk_ids, 4 * n)) return QMOE_ERR_ALIAS;
+        if (need > 0 && overlap(outs[i], outn[i], ws, need)) return QMOE_ERR_ALIAS;
+        for (int j = i + 1; j < 5; j++)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return QMOE_ERR_ALIAS;
+    }
+    Worklist wl{};
+    wl.counts = counts;
+    wl.offsets = offsets;
+    wl.pairs = pairs;
+    wl.inv = inv;
+    wl.n_invalid = n_invalid;
+    wl.tile_m = MFMA_BM;
+    return status_of(launch_worklist(topk_ids, (int)n, k, experts, wl,
+                                     static_cast<int32_t *>(ws), as_stream(stream)));
+}
+
+size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens, int32_t k,
+                                  int32_t x_dtype) {
+    if (!desc || tokens < 0 || k < 1 || desc->experts < 1) return 0;
+    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return 0;
+    return (size_t)carve_layer(nullptr, desc->experts, desc->hidden, desc->inter, tokens, k,
+                               x_dtype)
+        .bytes;
+}
+
+int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens, int32_t k,
+                         int32_t x_dtype, qmoe_layer_ws_view *view) {
+    if (!desc || !view) return QMOE_ERR_NULL;
+    if (view->struct_size != sizeof(qmoe_layer_ws_view)) return QMOE_ERR_ABI;
+    if (tokens < 0 || k < 1 || desc->experts < 1) return QMOE_ERR_SHAPE;
+    const LayerWs L =
+        carve_layer(nullptr, desc->experts, desc->hidden, desc->inter, tokens, k, x_dtype);
+    *view = L.view;
+    return QMOE_OK;
+}
+
+int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int32_t tokens,
+               const int32_t *topk_ids, const float *topk_w, int32_t k, float *out, void *ws,
+               size_t ws_bytes, void *stream) {
+    int s = check_layer_desc(desc);
+    if (s) return s;
+    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (tokens < 0 || k < 1 || k > MAX_TOPK) return QMOE_ERR_SHAPE;
+    if ((int64_t)tokens * k > (int64_t)1 << 30) return QMOE_ERR_SHAPE;
+    const int E = desc->experts, H = desc->hidden, F = desc->inter;
+    if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
+        return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype == QMOE_BF16 && H % 128 != 0) return QMOE_ERR_UNSUPPORTED;
+    {
+        const int64_t n0 = (int64_t)tokens * k;
+        const int64_t tiles = (n0 + MFMA_BM - 1) / MFMA_BM + (n0 < E ? n0 : E);
+        if (tiles > 65535) return QMOE_ERR_SHAPE;   // grid.y bound of the tiled kernels
+    }
+    if (tokens == 0) return QMOE_OK;
+    if (!x || !topk_ids || !topk_w || !out) return QMOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out)) return QMOE_ERR_ALIGN;
+    if (!aligned4(topk_ids) || !aligned4(topk_w)) return QMOE_ERR_ALIGN;
+    const LayerWs need = carve_layer(nullptr, E, H, F, tokens, k, x_dtype);
+    if (!ws || (int64_t)ws_bytes < need.bytes) return QMOE_ERR_WORKSPACE;
+    if (!aligned16(ws)) return QMOE_ERR_ALIGN;
+    const int64_t n = (int64_t)tokens * k;
+    const int64_t xb = (int64_t)tokens * H * (x_dtype == QMOE_F32 ? 4 : 2);
+    const int64_t ob = (int64_t)tokens * H * 4;
+    if (overlap(out, ob, x, xb) || overlap(out, ob, topk_ids, 4 * n) ||
+        overlap(out, ob, topk_w, 4 * n) || overlap(out, ob, ws, need.bytes) ||
+        overlap(ws, need.bytes, x, xb) || overlap(ws, need.bytes, topk_ids, 4 * n) ||
+        overlap(ws, need.bytes, topk_w, 4 * n))
+        return QMOE_ERR_ALIAS;
+
+    const LayerWs L = carve_layer(ws, E, H, F, tokens, k, x_dtype);
+    const hipStream_t st = as_stream(stream);
+    const QMat G = to_qmat(&desc->gate), U = to_qmat(&desc->up), D = to_qmat(&desc->down);
+    hipError_t e;
+    if (x_dtype == QMOE_F32) {
+        Worklist wl = L.wl;
+        wl.tiles = nullptr;
+        wl.n_tiles = nullptr;
+        e = launch_decode_prep(topk_ids, (int)n, k, E, wl, static_cast<const float *>(x), tokens,
+                               H, L.xd, out, st);
+        GemvRoute r{};
+        r.wl = wl;
+        r.topk_w = topk_w;
+        r.k = k;
+        r.max_active = L.max_active;
+        if (e == hipSuccess) e = launch_gemv_gateup(G, U, L.xd, L.hd, r, st);
+        if (e == hipSuccess) e = launch_gemv_down(D, L.hd, out, r, st);
+    } else {
+        e = launch_worklist(topk_ids, (int)n, k, E, L.wl, L.hist, st);
+        MfmaRoute r{};
+        r.wl = L.wl;
+        r.topk_w = topk_w;
+        r.k = k;
+        r.max_tiles = L.max_tiles;
+        if (e == hipSuccess)
+            e = launch_mfma_gateup(G, U, static_cast<const uint16_t *>(x), L.h16, r, st);
+        if (e == hipSuccess) e = launch_mfma_down(D, L.h16, L.y, r, st);
+        if (e == hipSuccess) e = launch_combine(L.y, L.wl.inv, tokens, k, H, out, st);
+    }
+    return status_of(e);
+}
+
+}  // extern "C"

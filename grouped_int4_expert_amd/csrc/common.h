@@ -1,0 +1,112 @@
+// Device-side helpers shared by the qmoe HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QMOE_WAVE 64
+
+namespace qmoe {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
+
+// Lanes per wave and the lane index.
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (QMOE_WAVE - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / QMOE_WAVE; }
+
+// Butterfly sum over groups of `width` consecutive lanes (width a power of
+// two, <= 64); every lane of a group ends with the group's sum.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, QMOE_WAVE);
+    return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, QMOE_WAVE));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+    for (int o = QMOE_WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, QMOE_WAVE);
+    return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, QMOE_WAVE);
+    return v;
+}
+
+// Signed int4 x int4 dot of 8 nibbles, accumulated into c (v_dot8_i32_i4).
+__device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+}
+
+// Byte permute: result byte i = byte sel_i of the 8-byte value {hi:lo}.
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// Activation digits ("x digits").  A 32-element chunk of an f32 activation
+// row is carried as a block fixed-point integer v_i = rint(x_i * 2^(18-E))
+// (2^(E-1) <= max|x| < 2^E), written in five balanced base-16 digits
+// d_k in [-8, 7] (v = sum_k d_k 16^k) so that a packed int4 weight nibble
+// and a digit nibble multiply exactly in v_dot8_i32_i4.  Layout of one row
+// of I elements: I/32 chunks x 5 planes x 4 dwords (plane k, dword d holds
+// the digits of chunk elements 8d..8d+7, element 8d+i in nibble i), plus one
+// f32 factor 2^(E-18) per chunk in a separate array.  |v| <= 2^18 fits the
+// five-digit range [-559240, 489335].
+// ---------------------------------------------------------------------------
+constexpr int XD_PLANES = 5;
+constexpr int XD_CHUNK = 32;                       // elements per factor
+constexpr int XD_DWORDS = XD_PLANES * 4;           // dwords per chunk
+constexpr int XD_FRAC_BITS = 18;
+
+// Quantise one chunk held one element per lane by 32 consecutive lanes
+// (lanes with `valid` false hold zero).  Lane (8d + i) of the chunk gets its
+// five digit nibbles; returns the factor.  Writes plane dwords through
+// `store(plane, dword, value)` from lanes with (lane % 8) == 0.
+template <typename Store>
+__device__ __forceinline__ float quantise_chunk32(float x, Store store) {
+    const float m = group_max<32>(fabsf(x));
+    float factor;
+    int v = 0;
+    if (!(m <= 3.0e38f)) {                    // inf or nan in the chunk
+        factor = __int_as_float(0x7fc00000);
+    } else if (m == 0.0f) {
+        factor = 0.0f;
+    } else {
+        int e;
+        frexpf(m, &e);                        // m = f * 2^e, f in [0.5, 1)
+        v = (int)rintf(ldexpf(x, XD_FRAC_BITS - e));
+        factor = ldexpf(1.0f, e - XD_FRAC_BITS);
+    }
+    const int sub = lane_id() & 7;            // element inside the dword
+    const int dw = (lane_id() & 31) >> 3;     // dword inside the plane
+#pragma unroll
+    for (int k = 0; k < XD_PLANES; k++) {
+        const int d = ((v + 8) & 15) - 8;
+        v = (v - d) >> 4;
+        uint32_t nib = (uint32_t)(d & 15) << (4 * sub);
+        nib = group_or<8>(nib);
+        if (sub == 0) store(k, dw, nib);
+    }
+    return factor;
+}
+
+}  // namespace qmoe

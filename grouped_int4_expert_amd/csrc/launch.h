@@ -1,0 +1,99 @@
+// Internal launchers of the qmoe kernels (host side).  Shapes are validated
+// by the C ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// Packed int4 matrix stack on the device (see include/qmoe.h).
+struct QMat {
+    const uint8_t *q;
+    const float *s;
+    int64_t q_stride;   // bytes between experts
+    int64_t s_stride;   // floats between experts
+    int rows, cols;     // O, I (cols % 64 == 0)
+};
+
+// Worklist outputs inside a workspace.
+struct Worklist {
+    int32_t *counts;    // [E]
+    int32_t *offsets;   // [E+1]
+    int32_t *pairs;     // [n]
+    int32_t *inv;       // [n]
+    int32_t *n_invalid; // [1]
+    int32_t *active;    // [E]  experts with a pair, ascending (nullable)
+    int32_t *n_active;  // [1]                                 (nullable)
+    int32_t *tiles;     // [2*max_tiles] (expert, first row)   (nullable)
+    int32_t *n_tiles;   // [1]                                 (nullable)
+    int tile_m;         // rows per tile
+};
+
+// Decode activation digits of `rows` rows of width `cols` (see common.h).
+struct XDigits {
+    uint32_t *dig;      // [rows][cols/32][20]
+    float *fac;         // [rows][cols/32]
+};
+
+hipError_t launch_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
+                       int32_t *n_bad, hipStream_t st);
+hipError_t launch_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
+                         hipStream_t st);
+
+// Worklist for n = tokens*k pairs.  block_counts: scratch of
+// wl_scratch_ints(n, E) int32 (unused when n is small).
+int64_t wl_scratch_ints(int64_t n, int E);
+hipError_t launch_worklist(const int32_t *ids, int n, int k, int E, const Worklist &wl,
+                           int32_t *scratch, hipStream_t st);
+
+// Decode preparation in one launch: the worklist (block 0), x -> digits for
+// all tokens, and out <- 0.
+hipError_t launch_decode_prep(const int32_t *ids, int n, int k, int E, const Worklist &wl,
+                              const float *x, int tokens, int hidden, XDigits xd, float *out,
+                              hipStream_t st);
+
+// x -> digits only (matvec and the single-expert FFN).
+hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStream_t st);
+
+// Decode GEMVs.  Tokens of expert `active[a]` are the sorted positions
+// offsets[e]..offsets[e+1]; in "direct" mode (wl.pairs == nullptr) there is
+// one expert (0) with positions 0..ntok-1 = tokens 0..ntok-1, weight 1.
+struct GemvRoute {
+    Worklist wl;
+    const float *topk_w;   // [n] routing weights (down, routed mode)
+    int k;                 // top-k (pair -> token)
+    int max_active;        // grid bound on active experts
+    int ntok;              // direct mode: tokens
+};
+
+// h digits for the down projection: silu(gate x) * (up x) per sorted pair.
+hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDigits hd,
+                              const GemvRoute &r, hipStream_t st);
+// out[t] += w * down(h) (routed: atomic adds; direct: plain stores).
+hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const GemvRoute &r,
+                            hipStream_t st);
+// y = W x for `batch` rows of digits.
+hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
+                              hipStream_t st);
+
+// Prefill (bf16 activations, MFMA).
+constexpr int MFMA_BM = 128;
+struct MfmaRoute {
+    Worklist wl;
+    const float *topk_w;
+    int k;
+    int max_tiles;     // grid bound on tiles
+    int ntok;          // direct mode
+};
+// h16[pos][F] = silu(G x) * (U x) as f16, pos = sorted pair position.
+hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *x_bf16,
+                              uint16_t *h16, const MfmaRoute &r, hipStream_t st);
+// Y[pos][H] = w * (D h) in f32 (direct mode: out[t] = D h).
+hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y,
+                            const MfmaRoute &r, hipStream_t st);
+// out[t] = sum_j Y[inv[t*k + j]] (dropped pairs skipped).
+hipError_t launch_combine(const float *y, const int32_t *inv, int tokens, int k, int hidden,
+                          float *out, hipStream_t st);
+
+}  // namespace qmoe

@@ -1,0 +1,83 @@
+// Packing of int8 codes into the grouped int4 container and back.
+//
+// Format (colibri pull request "cuda+engine: full fmt=4 (grouped int4 gs=64)
+// support", Summary: int4 rows are (I+1)/2 bytes, same nibble layout as the
+// per-row format; comment "implementation complete but system-instability":
+// the container holds unsigned offset nibbles 0..15): byte j of a row holds
+// element 2j in its low nibble and 2j+1 in its high nibble, each as q + 8.
+#include "common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+// One thread per output byte; grid-stride over rows*row_bytes bytes.
+__global__ void pack_kernel(const int8_t *__restrict__ q, int64_t rows, int64_t cols,
+                            uint8_t *__restrict__ packed, int32_t *__restrict__ n_bad) {
+    const int64_t rb = (cols + 1) / 2;
+    const int64_t total = rows * rb;
+    int bad = 0;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = idx / rb, j = idx - o * rb;
+        const int64_t i0 = 2 * j;
+        const int v0 = q[o * cols + i0];
+        bad += (v0 < -8 || v0 > 7);
+        uint32_t b = (uint32_t)(v0 + 8) & 15u;
+        uint32_t hi = 8u;                       // pad nibble: value 0
+        if (i0 + 1 < cols) {
+            const int v1 = q[o * cols + i0 + 1];
+            bad += (v1 < -8 || v1 > 7);
+            hi = (uint32_t)(v1 + 8) & 15u;
+        }
+        packed[idx] = (uint8_t)(b | (hi << 4));
+    }
+    if (n_bad) {
+        bad = wave_sum_i32(bad);
+        if (lane_id() == 0 && bad) atomicAdd(n_bad, bad);
+    }
+}
+
+__global__ void unpack_kernel(const uint8_t *__restrict__ packed, int64_t rows, int64_t cols,
+                              int8_t *__restrict__ q) {
+    const int64_t rb = (cols + 1) / 2;
+    const int64_t total = rows * rb;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t o = idx / rb, j = idx - o * rb;
+        const uint32_t b = packed[idx];
+        q[o * cols + 2 * j] = (int8_t)((int)(b & 15u) - 8);
+        if (2 * j + 1 < cols) q[o * cols + 2 * j + 1] = (int8_t)((int)(b >> 4) - 8);
+    }
+}
+
+__global__ void zero_i32_kernel(int32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+static int grid_for(int64_t n, int block) {
+    int64_t g = (n + block - 1) / block;
+    if (g > 65536) g = 65536;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+hipError_t launch_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
+                       int32_t *n_bad, hipStream_t st) {
+    if (n_bad) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, st, n_bad, (int64_t)1);
+    const int64_t total = rows * ((cols + 1) / 2);
+    hipLaunchKernelGGL(pack_kernel, dim3(grid_for(total, 256)), dim3(256), 0, st, q, rows,
+                       cols, packed, n_bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
+                         hipStream_t st) {
+    const int64_t total = rows * ((cols + 1) / 2);
+    hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(total, 256)), dim3(256), 0, st, packed,
+                       rows, cols, q);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

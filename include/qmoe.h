@@ -1,0 +1,207 @@
+/*
+ * qmoe -- grouped int4 (gs = 64) MoE expert matmul for AMD Instinct MI355X
+ * (gfx950).  C ABI of libqmoe.so.
+ *
+ * The operation is the one the colibri pull request "cuda+engine: full fmt=4
+ * (grouped int4 gs=64) support + diagnostic harness" adds to its engine:
+ * expert weights quantised to signed int4, packed two per byte, with one f32
+ * scale for every 64 consecutive input elements of a row (Summary and
+ * Problem), evaluated as the fused gate+up pair (x read once for both
+ * matrices) followed by the down projection (Summary, "matmul_i4_grouped_pair"
+ * and "expert_gate_up"), over a top-k token-to-expert table that is built on
+ * the device (pxq_llama.cpp release notes, "Device-side MoE row map").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library never allocates, frees or synchronises.  Work is enqueued on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and the
+ *    return value comes from host-side checks made before anything is
+ *    enqueued.  A non-zero status means nothing was launched ("refuses
+ *    rather than guessing": the fail-closed launcher guard of the same pull
+ *    request, comment "implementation complete but system-instability").
+ *  - The library is stateless and thread-safe.  Concurrent calls on one
+ *    stream serialise; calls on different streams that share a workspace
+ *    race.
+ *  - Sizes are 64-bit where they count bytes.  Shapes are int32.
+ *  - Packed int4 layout ("qmat"): row-major [rows][ceil(cols/2)] bytes;
+ *    element 2j of a row sits in the LOW nibble of byte j and element 2j+1
+ *    in the high nibble; a nibble u stores the code q = u - 8 (offset
+ *    binary, as the container on the pages stores it; XOR 0x88 per byte
+ *    gives two's complement).  Scales are row-major f32 [rows][ceil(cols/g)]
+ *    with scale(o, i) = s[o * ng + i / g] (comment "blocked by GPU driver
+ *    instability": scales[o*ng + i/gs]).
+ *  - GPU kernels accept group == 64 and cols % 64 == 0 only; other values
+ *    return QMOE_ERR_UNSUPPORTED.  Every pointer must be 16-byte aligned
+ *    (QMOE_ERR_ALIGN otherwise), like the vector-load guard of the
+ *    pxq_llama.cpp notes (release rc3 fixes) that declines rather than
+ *    faults.
+ *  - Bad expert ids (outside [0, E)) are data, not arguments: they are
+ *    dropped (contribute zero) and counted into an int32 on the device.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+    QMOE_OK = 0,
+    QMOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    QMOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    QMOE_ERR_ALIGN = 3,       /* a pointer or stride is not 16-byte aligned */
+    QMOE_ERR_UNSUPPORTED = 4, /* valid for the format, not for these kernels */
+    QMOE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+    QMOE_ERR_ALIAS = 6,       /* an output overlaps an input */
+    QMOE_ERR_ABI = 7,         /* struct_size does not match this library */
+    QMOE_ERR_HIP = 8          /* a kernel launch failed (hipGetLastError) */
+};
+
+/* Activation dtypes.  The dtype of x selects the path: f32 = decode (GEMV
+ * kernels), bf16 = prefill (grouped MFMA kernels). */
+enum { QMOE_F32 = 0, QMOE_BF16 = 1 };
+
+/* One int4-g64 matrix, or a stack of per-expert matrices of one shape.
+ * q_expert_stride is the byte distance between experts' packed codes and
+ * s_expert_stride the float distance between their scales (0 for a single
+ * matrix).  Both must keep every expert 16-byte aligned. */
+typedef struct qmoe_qmat {
+    uint32_t struct_size;     /* = sizeof(qmoe_qmat) */
+    int32_t rows;             /* O: output features */
+    int32_t cols;             /* I: input features */
+    int32_t group;            /* g: inputs per scale (64) */
+    const uint8_t *q;         /* packed codes, [E][rows][cols/2] bytes */
+    const float *s;           /* scales, [E][rows][cols/group] f32 */
+    int64_t q_expert_stride;  /* bytes between experts */
+    int64_t s_expert_stride;  /* floats between experts */
+} qmoe_qmat;
+
+/* A MoE layer: E experts of hidden H and intermediate F.  gate and up are
+ * [E][F][H], down is [E][H][F]. */
+typedef struct qmoe_layer_desc {
+    uint32_t struct_size;     /* = sizeof(qmoe_layer_desc) */
+    int32_t experts;          /* E, 1..1024 */
+    int32_t hidden;           /* H */
+    int32_t inter;            /* F */
+    int32_t group;            /* 64 */
+    qmoe_qmat gate, up, down;
+} qmoe_layer_desc;
+
+/* QMOE_ABI_VERSION of the loaded library; a caller built against another
+ * version must not call anything else (the pull request's 7-vs-8-argument
+ * upload mismatch, comment "fmt=4 CUDA attention crash", is the failure this
+ * guards against). */
+int qmoe_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *qmoe_status_str(int status);
+
+/* rows * ceil(cols / 2): bytes of one packed matrix (pull request Summary:
+ * int4 row_bytes = (I + 1) / 2).  Returns 0 for negative sizes. */
+size_t qmoe_packed_bytes(int64_t rows, int64_t cols);
+
+/* rows * ceil(cols / group): f32 scales of one matrix (pull request Summary:
+ * O*ng scales instead of O).  Returns 0 for a non-positive group. */
+size_t qmoe_scale_count(int64_t rows, int64_t cols, int64_t group);
+
+/* Pack int8 codes q [rows][cols] (row-major, device) into the packed layout
+ * above: byte j of row o = (q[o][2j] + 8) & 15 | ((q[o][2j+1] + 8) & 15) << 4,
+ * pad nibble 8 when cols is odd.  Codes outside [-8, 7] are stored wrapped
+ * and, when n_bad != NULL, counted into *n_bad (a device int32 the call
+ * zeroes first).  The offset encoding is the container's ("unsigned offset
+ * encoding (0-15)", comment "implementation complete but
+ * system-instability").  Requires cols even and packed 16-byte aligned rows
+ * (cols % 32 == 0); q only 1-byte aligned. */
+int qmoe_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
+              int32_t *n_bad, void *stream);
+
+/* Inverse of qmoe_pack: packed -> int8 codes in [-8, 7].  A test aid. */
+int qmoe_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
+                void *stream);
+
+/* Workspace bytes qmoe_matvec needs for `batch` rows of x. */
+size_t qmoe_matvec_workspace_bytes(const qmoe_qmat *W, int32_t batch);
+
+/* y[b][o] = sum_i s[o][i/64] * q[o][i] * x[b][i] for b < batch: the single
+ * grouped int4 matvec ("quant_matmul" with per-group scale, pull request
+ * Summary).  x f32 [batch][cols], y f32 [batch][rows]; y must not overlap x
+ * or the workspace.  W->q_expert_stride is ignored (expert 0). */
+int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes qmoe_expert_ffn needs. */
+size_t qmoe_expert_ffn_workspace_bytes(const qmoe_qmat *gate,
+                                       const qmoe_qmat *up,
+                                       const qmoe_qmat *down, int32_t x_dtype,
+                                       int32_t batch);
+
+/* One expert: out[b] = down(silu(gate x_b) * (up x_b)), silu(z) =
+ * z / (1 + exp(-z)).  gate/up are [F][H], down is [H][F] (expert 0 of each
+ * descriptor).  x is f32 or bf16 [batch][H] per x_dtype; out is f32
+ * [batch][H] and must not overlap x.  The fused pair reads x once for both
+ * matrices (pull request Summary, "matmul_i4_grouped_pair: fused gate+up ...
+ * reads x once instead of twice"). */
+int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up,
+                    const qmoe_qmat *down, int32_t x_dtype, const void *x,
+                    int32_t batch, float *out, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Token-to-expert table for one batched MoE layer, built entirely on the
+ * device with no host round trip (pxq_llama.cpp notes, "Device-side MoE row
+ * map": histogram, scan and fill).  Input topk_ids int32 [tokens][k].
+ * Outputs (device int32):
+ *   counts[experts]      valid pairs per expert;
+ *   offsets[experts+1]   exclusive scan of counts, offsets[E] = n_valid;
+ *   pairs[tokens*k]      pair ids p = t*k + j grouped by expert (ascending
+ *                        expert, ascending p inside one expert), -1 after
+ *                        the n_valid entries;
+ *   inv[tokens*k]        position of pair p in `pairs`, -1 if dropped;
+ *   n_invalid[1]         number of ids outside [0, experts).
+ * The result is unique (a stable counting sort), so it is bit-exact against
+ * any correct builder.  ws/ws_bytes: scratch from
+ * qmoe_worklist_workspace_bytes (may be 0 bytes for small inputs). */
+size_t qmoe_worklist_workspace_bytes(int32_t tokens, int32_t k,
+                                     int32_t experts);
+int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k,
+                  int32_t experts, int32_t *counts, int32_t *offsets,
+                  int32_t *pairs, int32_t *inv, int32_t *n_invalid, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* Workspace bytes qmoe_layer needs for these sizes and dtype. */
+size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
+                                  int32_t k, int32_t x_dtype);
+
+/* The routed MoE layer:
+ *   out[t] = sum_{j<k} topk_w[t][j] * ffn_{topk_ids[t][j]}(x_t)
+ * x is [tokens][H] f32 (decode path) or bf16 (prefill path); topk_ids int32
+ * and topk_w f32 are [tokens][k]; out is f32 [tokens][H], fully written,
+ * and must not overlap x, the routing arrays or the workspace.  Routing is
+ * an input: the layer does not pick experts.  Ids outside [0, E) are
+ * dropped.  After the call the workspace begins with the worklist in the
+ * layout of qmoe_layer_ws_view (for inspection and tests).  Each expert's
+ * weights are streamed once per call on the decode path (all of that
+ * expert's tokens share the pass). */
+int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+               int32_t tokens, const int32_t *topk_ids, const float *topk_w,
+               int32_t k, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Byte offsets, inside a qmoe_layer workspace, of the worklist arrays the
+ * call leaves behind (counts, offsets, pairs, inv, n_invalid). */
+typedef struct qmoe_layer_ws_view {
+    uint32_t struct_size;
+    int64_t counts, offsets, pairs, inv, n_invalid;
+} qmoe_layer_ws_view;
+int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens,
+                         int32_t k, int32_t x_dtype, qmoe_layer_ws_view *view);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

@@ -1,0 +1,159 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every entry
+point include/qmoe.h declares, reports its ABI version and size formulas, and
+rejects bad arguments before any HIP call (no kernel is ever launched here:
+every call below fails validation, which runs first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import grouped_int4_expert_amd as q
+from grouped_int4_expert_amd import qmoe_layer_desc, qmoe_qmat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return q.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(q.EXPORTS)
+
+
+def test_abi_version_and_status(lib):
+    assert lib.qmoe_abi_version() == q.ABI_VERSION == 1
+    for s in range(9):
+        assert q.qmoe_status_str(s)
+    assert q.qmoe_status_str(999) == "unknown status"
+
+
+def test_size_formulas(lib):
+    # kv_b header of the pull request: 28,672 rows x 256 B, 8 scales per row
+    assert q.qmoe_packed_bytes(28672, 512) == 7340032
+    assert q.qmoe_scale_count(28672, 512, 64) == 229376
+    assert q.qmoe_packed_bytes(3, 5) == 9
+    assert q.qmoe_scale_count(3, 5, 2) == 9
+    assert q.qmoe_packed_bytes(-1, 4) == 0
+    assert q.qmoe_scale_count(4, 4, 0) == 0
+
+
+FAKE = 1 << 40   # a 16-byte aligned address that is never dereferenced
+
+
+def qmat(rows, cols, group=64, q_=FAKE, s_=FAKE + (1 << 30), qs=0, ss=0, size=None):
+    m = qmoe_qmat()
+    m.struct_size = ctypes.sizeof(qmoe_qmat) if size is None else size
+    m.rows, m.cols, m.group = rows, cols, group
+    m.q, m.s = q_, s_
+    m.q_expert_stride, m.s_expert_stride = qs, ss
+    return m
+
+
+def layer_desc(E=4, H=256, F=128, group=64, size=None):
+    d = qmoe_layer_desc()
+    d.struct_size = ctypes.sizeof(qmoe_layer_desc) if size is None else size
+    d.experts, d.hidden, d.inter, d.group = E, H, F, group
+    step = 1 << 32
+    d.gate = qmat(F, H, group, FAKE, FAKE + step, F * H // 2, F * H // 64)
+    d.up = qmat(F, H, group, FAKE + 2 * step, FAKE + 3 * step, F * H // 2, F * H // 64)
+    d.down = qmat(H, F, group, FAKE + 4 * step, FAKE + 5 * step, H * F // 2, H * F // 64)
+    return d
+
+
+def call_layer(lib, d, dtype=0, x=FAKE + (6 << 32), T=2, ids=FAKE + (7 << 32),
+               w=FAKE + (8 << 32), k=2, out=FAKE + (9 << 32), ws=FAKE + (10 << 32),
+               ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.qmoe_layer_workspace_bytes(ctypes.byref(d), T, k, dtype)
+    return lib.qmoe_layer(ctypes.byref(d), dtype, x, T, ids, w, k, out, ws, ws_bytes, None)
+
+
+def test_layer_rejections(lib):
+    d = layer_desc()
+    assert call_layer(lib, layer_desc(size=8)) == 7                     # ABI
+    d2 = layer_desc()
+    d2.gate.struct_size = 4
+    assert call_layer(lib, d2) == 7
+    assert call_layer(lib, layer_desc(group=128)) == 4                  # UNSUPPORTED
+    assert call_layer(lib, layer_desc(H=200)) == 4
+    assert call_layer(lib, layer_desc(E=0)) == 2                        # SHAPE
+    assert call_layer(lib, layer_desc(E=2000)) == 2
+    assert call_layer(lib, d, dtype=7) == 4
+    assert call_layer(lib, d, k=0) == 2
+    assert call_layer(lib, d, x=None) == 1                              # NULL
+    assert call_layer(lib, d, out=None) == 1
+    assert call_layer(lib, d, x=FAKE + 4) == 3                          # ALIGN
+    assert call_layer(lib, d, ids=FAKE + 2) == 3
+    assert call_layer(lib, d, ws=None) == 5                             # WORKSPACE
+    assert call_layer(lib, d, ws_bytes=16) == 5
+    assert call_layer(lib, d, out=FAKE + (6 << 32)) == 6                # ALIAS out == x
+    assert call_layer(lib, d, ws=FAKE + (9 << 32)) == 6                 # ws == out
+    assert call_layer(lib, d, T=0) == 0                                 # nothing to do
+    d3 = layer_desc()
+    d3.down.rows = 128
+    assert call_layer(lib, d3) == 2
+    d4 = layer_desc()
+    d4.up.q = FAKE + 8
+    assert call_layer(lib, d4) == 3
+    d5 = layer_desc()
+    d5.gate.q_expert_stride = 16
+    assert call_layer(lib, d5) == 2
+    d6 = layer_desc()
+    d6.gate.s = None
+    assert call_layer(lib, d6) == 1
+
+
+def test_matvec_and_pack_rejections(lib):
+    W = qmat(256, 1024)
+    nb = lib.qmoe_matvec_workspace_bytes(ctypes.byref(W), 1)
+    assert nb > 0
+    ws = FAKE + (20 << 32)
+    assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1000)), FAKE, 1, FAKE + (30 << 32), ws, nb,
+                           None) == 4
+    assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1024, size=3)), FAKE, 1, FAKE, ws, nb,
+                           None) == 7
+    assert lib.qmoe_matvec(ctypes.byref(W), None, 1, FAKE + (30 << 32), ws, nb, None) == 1
+    assert lib.qmoe_matvec(ctypes.byref(W), FAKE + 8, 1, FAKE + (30 << 32), ws, nb, None) == 3
+    assert lib.qmoe_matvec(ctypes.byref(W), FAKE + (40 << 32), 1, FAKE + (30 << 32), ws, 8,
+                           None) == 5
+    assert lib.qmoe_matvec(ctypes.byref(W), FAKE + (40 << 32), 1, FAKE + (40 << 32), ws, nb,
+                           None) == 6
+    assert lib.qmoe_matvec(ctypes.byref(W), FAKE, 0, FAKE, ws, nb, None) == 0
+    assert lib.qmoe_pack(None, 4, 4, FAKE, None, None) == 1
+    assert lib.qmoe_pack(FAKE, -1, 4, FAKE, None, None) == 2
+    assert lib.qmoe_pack(FAKE, 4, 64, FAKE + 8, None, None) == 6       # packed overlaps q
+    assert lib.qmoe_pack(FAKE, 0, 4, FAKE, None, None) == 0
+    assert lib.qmoe_worklist(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 2
+    assert lib.qmoe_worklist(FAKE, 4, 2, 8, None, FAKE, FAKE, FAKE, FAKE, None, 0, None) == 1
+    a = FAKE + (50 << 32)
+    assert lib.qmoe_worklist(FAKE, 4, 2, 8, a, a, a + 4096, a + 8192, a + 12288, None, 0,
+                             None) == 6
+
+
+def test_expert_ffn_rejections(lib):
+    G, U, D = qmat(128, 256), qmat(128, 256), qmat(256, 128)
+    nb = lib.qmoe_expert_ffn_workspace_bytes(ctypes.byref(G), ctypes.byref(U), ctypes.byref(D),
+                                             0, 2)
+    ws = FAKE + (20 << 32)
+    args = lambda x_dtype, x, out: lib.qmoe_expert_ffn(  # noqa: E731
+        ctypes.byref(G), ctypes.byref(U), ctypes.byref(D), x_dtype, x, 2, out, ws, nb, None)
+    assert args(3, FAKE, FAKE + (30 << 32)) == 4
+    assert args(0, None, FAKE + (30 << 32)) == 1
+    assert args(0, FAKE + (30 << 32), FAKE + (30 << 32)) == 6
+    D2 = qmat(256, 192)
+    assert lib.qmoe_expert_ffn(ctypes.byref(G), ctypes.byref(U), ctypes.byref(D2), 0, FAKE, 2,
+                               FAKE + (30 << 32), ws, nb, None) == 2

@@ -1,0 +1,238 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same
+seeded inputs.  Integer work (pack, worklist) is bit-exact; floating outputs
+meet relative L2 <= 1e-4 on the f32 (decode) path and <= 2e-3 on the bf16
+(prefill, MFMA) path.  Full-size layers are checked on sampled tokens the
+oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_int4_expert_amd as qm
+import synth
+from gpu_util import BF16_TOL, F32_TOL, Layer, orc, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qm.load()
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ pack ---
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 5), (7, 64), (33, 4097), (256, 1024)])
+def test_pack_bit_exact(rows, cols):
+    say(f"pack {rows}x{cols}")
+    g = synth.generator(100 + rows + cols)
+    q = synth.rand_q(g, (rows, cols))
+    ref, bad = orc().pack(q.numpy())
+    got = qm.qmoe_pack(q.to(DEV))
+    assert np.array_equal(got.cpu().numpy(), ref)
+    back = qm.qmoe_unpack(got, cols)
+    assert torch.equal(back.cpu(), q)
+
+
+def test_pack_counts_out_of_range():
+    say("pack out of range")
+    q = torch.tensor([[8, -9, 0, 7, 127, -128]], dtype=torch.int8)
+    ref, bad = orc().pack(q.numpy())
+    got, nbad = qm.qmoe_pack(q.to(DEV), count_bad=True)
+    assert np.array_equal(got.cpu().numpy(), ref)
+    assert int(nbad.item()) == bad == 4
+
+
+def test_pack_all_bytes_roundtrip():
+    say("unpack all bytes")
+    allb = torch.arange(256, dtype=torch.uint8).reshape(256, 1)
+    got = qm.qmoe_unpack(allb.to(DEV), 2).cpu().numpy()
+    assert np.array_equal(got, orc().unpack(allb.numpy(), 2))
+
+
+# -------------------------------------------------------------- worklist ---
+
+def _wl_check(ids, E):
+    ref = orc().worklist(ids.numpy(), E)
+    got = qm.qmoe_worklist(ids.to(DEV), E)
+    for key in ("counts", "offsets", "pairs", "inv"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    assert int(got["n_invalid"].item()) == ref["n_invalid"]
+
+
+def test_worklist_64_random_cases():
+    rng = np.random.default_rng(7)
+    for case in range(64):
+        T = int(rng.integers(0, 300))
+        k = int(rng.integers(1, 9))
+        E = int(rng.integers(1, 300))
+        ids = torch.from_numpy(rng.integers(-2, E + 2, size=(T, k)).astype(np.int32))
+        say(f"worklist case {case}: T={T} k={k} E={E}")
+        _wl_check(ids, E)
+
+
+@pytest.mark.parametrize("T,k,E", [(8192, 8, 128), (2048, 8, 256), (5000, 3, 1024),
+                                   (4096, 2, 1)])
+def test_worklist_large_multiblock(T, k, E):
+    say(f"worklist large T={T} k={k} E={E}")
+    g = synth.generator(T + E)
+    logits = torch.rand((T, E), generator=g)
+    ids, _ = synth.route_topk_fast(logits, min(k, E))
+    if ids.shape[1] < k:
+        ids = ids.repeat(1, k)[:, :k].contiguous()
+    ids[::97, 0] = -1          # a sprinkle of dropped ids
+    ids[::89, -1] = E
+    _wl_check(ids, E)
+
+
+# ---------------------------------------------------------------- matvec ---
+
+def _matvec_inputs(rows, cols, seed, batch=1):
+    g = synth.generator(seed)
+    q = synth.rand_q(g, (rows, cols))
+    s = synth.rand_scales(g, (rows, cols // 64))
+    x = synth.rand_x(g, (batch, cols))
+    return q, s, x
+
+
+def test_matvec_one_hot_bit_exact():
+    """x = e_j: y[o] = fl(s[o, j/64] * q[o, j]) exactly, which pins nibble
+    order, offset and scale index in the kernel."""
+    rows, cols = 37, 192
+    q, s, _ = _matvec_inputs(rows, cols, 5)
+    pq = qm.qmoe_pack(q.to(DEV))
+    sd = s.to(DEV)
+    for j in (0, 1, 31, 32, 63, 64, 127, 130, 191):
+        say(f"matvec one-hot j={j}")
+        x = torch.zeros(1, cols)
+        x[0, j] = 1.0
+        y = qm.qmoe_matvec(pq, sd, cols, x.to(DEV)).cpu().numpy()[0]
+        want = (q[:, j].double().numpy() * s[:, j // 64].double().numpy()).astype(np.float32)
+        assert np.array_equal(y, want), j
+
+
+@pytest.mark.parametrize("rows,cols,batch,seed", [(256, 1024, 1, 0), (100, 320, 3, 9),
+                                                  (64, 6144, 2, 10), (513, 1536, 1, 11)])
+def test_matvec_random(rows, cols, batch, seed):
+    say(f"matvec {rows}x{cols} batch {batch}")
+    q, s, x = _matvec_inputs(rows, cols, seed, batch)
+    y = qm.qmoe_matvec(qm.qmoe_pack(q.to(DEV)), s.to(DEV), cols, x.to(DEV)).cpu().numpy()
+    pq, _ = orc().pack(q.numpy())
+    ref = orc().matvec(pq, s.numpy(), cols, x.numpy())
+    assert rel_l2(y, ref) <= F32_TOL
+
+
+# ------------------------------------------------------------ expert ffn ---
+
+@pytest.mark.parametrize("H,F,batch,dtype", [(4096, 1536, 1, "f32"), (4096, 1536, 1, "bf16"),
+                                             (256, 128, 5, "f32"), (256, 128, 130, "bf16")])
+def test_expert_ffn(H, F, batch, dtype):
+    say(f"expert ffn H={H} F={F} batch={batch} {dtype}")
+    L = Layer(1, H, F, seed=1)
+    x = synth.rand_x(L.gen, (batch, H))
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    out = qm.qmoe_expert_ffn(L.packed["qg"][0], L.s_dev["sg"][0], L.packed["qu"][0],
+                             L.s_dev["su"][0], L.packed["qd"][0], L.s_dev["sd"][0], H, F,
+                             x.to(DEV)).cpu().numpy()
+    st = L.oracle_subset([0])
+    ref = orc().ffn(st[0][0], st[1][0], st[2][0], st[3][0], st[4][0], st[5][0], H, F, x)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= tol
+
+
+# ----------------------------------------------------------------- layer ---
+
+def _layer_case(L, T, k, dtype, logits="normal", seed=0, tokens=None, mutate=None):
+    g = synth.generator(1000 + seed)
+    wl = synth.Workload("t", L.E, L.H, L.F, k, T, dtype, logits, seed)
+    x, ids, w = synth.layer_inputs(wl, g)
+    if mutate:
+        ids, w = mutate(ids, w)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref = L.oracle_layer(x, ids, w, tokens)
+    if tokens is not None:
+        out = out[np.asarray(tokens)]
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype,T,k", [("f32", 1, 4), ("f32", 37, 4), ("bf16", 37, 4),
+                                       ("bf16", 300, 4), ("f32", 300, 2)])
+def test_layer_small_full(dtype, T, k):
+    say(f"layer small E=16 H=256 F=128 T={T} k={k} {dtype}")
+    L = Layer(16, 256, 128, seed=21)
+    out, ref = _layer_case(L, T, k, dtype, seed=T)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_invalid_and_duplicate_ids(dtype):
+    say(f"layer invalid/duplicate ids {dtype}")
+    L = Layer(8, 256, 128, seed=22)
+
+    def mutate(ids, w):
+        ids = ids.clone()
+        ids[0, 0] = -1
+        ids[1, :] = 8          # every slot of token 1 invalid -> zero output
+        ids[2, 1] = ids[2, 0]  # a duplicate expert in one token
+        return ids, w
+    out, ref = _layer_case(L, 9, 3, dtype, seed=5, mutate=mutate)
+    assert np.all(out[1] == 0.0)
+    assert rel_l2(out, ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_layer_decode_e128(T):
+    say(f"decode layer E=128 H=4096 F=1536 T={T}")
+    L = _big_layer(128, 4096, 1536, 2)
+    toks = list(range(T)) if T <= 4 else [0, 5, 11, 15]
+    out, ref = _layer_case(L, T, 8, "f32", seed=T, tokens=toks)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= F32_TOL
+
+
+def test_layer_prefill_e128_t8192():
+    say("prefill layer E=128 H=4096 F=1536 T=8192")
+    L = _big_layer(128, 4096, 1536, 3)
+    toks = [0, 1, 777, 4096, 8191]
+    out, ref = _layer_case(L, 8192, 8, "bf16", logits="uniform", seed=3, tokens=toks)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= BF16_TOL
+
+
+_BIG = {}
+
+
+def _big_layer(E, H, F, seed):
+    key = (E, H, F, seed)
+    if key not in _BIG:
+        _BIG.clear()
+        torch.cuda.empty_cache()
+        _BIG[key] = Layer(E, H, F, seed=seed, gen_device=DEV)
+    return _BIG[key]
+
+
+def test_layer_worklist_left_in_workspace():
+    say("layer workspace worklist")
+    L = Layer(16, 256, 128, seed=23)
+    g = synth.generator(9)
+    wl = synth.Workload("t", 16, 256, 128, 4, 50, "f32", "normal", 9)
+    x, ids, w = synth.layer_inputs(wl, g)
+    for dtype, xx in ((qm.QMOE_F32, x), (qm.QMOE_BF16, x.to(torch.bfloat16))):
+        ws = torch.empty(L.dev.workspace_bytes(50, 4, dtype), dtype=torch.uint8, device=DEV)
+        qm.qmoe_layer(L.dev, xx.to(DEV), ids.to(DEV), w.to(DEV), ws=ws)
+        got = qm.layer_worklist_from_ws(L.dev, ws, 50, 4, dtype)
+        ref = orc().worklist(ids.numpy(), 16)
+        for key in ("counts", "offsets", "pairs", "inv"):
+            assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
