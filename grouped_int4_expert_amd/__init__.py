@@ -58,7 +58,7 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_pack", "qmoe_unpack", "qmoe_matvec_workspace_bytes", "qmoe_matvec",
            "qmoe_expert_ffn_workspace_bytes", "qmoe_expert_ffn",
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
-           "qmoe_layer", "qmoe_layer_ws_layout"]
+           "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout"]
 
 _lib = None
 
@@ -91,6 +91,9 @@ def load(path: str | None = None):
         "qmoe_layer_workspace_bytes": (sz, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32]),
         "qmoe_layer": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, vp,
                                       i32, vp, vp, sz, vp]),
+        "qmoe_layer_ex": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, vp,
+                                         i32, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_void_p),
+                                         i32]),
         "qmoe_layer_ws_layout": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32,
                                                 ctypes.POINTER(qmoe_layer_ws_view)]),
     }
@@ -319,6 +322,25 @@ def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=Non
     _check(load().qmoe_layer(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
                              _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
            "qmoe_layer")
+    return o
+
+
+def qmoe_layer_ex(layer: QLayer, x, topk_ids, topk_w, events, out=None, ws=None,
+                  stream=None):
+    """qmoe_layer that records the given torch.cuda.Event objects between its
+    phases (events[0] before the first kernel)."""
+    _dev(x, "x")
+    code = _dtype_code(x)
+    T, k = topk_ids.shape
+    o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
+                                                device=x.device)
+    nb = layer.workspace_bytes(T, k, code)
+    ws = _workspace(nb, x.device, ws)
+    handles = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(ev.cuda_event)
+                                                  for ev in events])
+    _check(load().qmoe_layer_ex(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
+                                _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(),
+                                _stream(stream), handles, len(events)), "qmoe_layer_ex")
     return o
 
 

@@ -367,6 +367,14 @@ int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens, int32_t k,
 int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int32_t tokens,
                const int32_t *topk_ids, const float *topk_w, int32_t k, float *out, void *ws,
                size_t ws_bytes, void *stream) {
+    return qmoe_layer_ex(desc, x_dtype, x, tokens, topk_ids, topk_w, k, out, ws, ws_bytes,
+                         stream, nullptr, 0);
+}
+
+int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int32_t tokens,
+                  const int32_t *topk_ids, const float *topk_w, int32_t k, float *out,
+                  void *ws, size_t ws_bytes, void *stream, void *const *phase_events,
+                  int32_t n_events) {
     int s = check_layer_desc(desc);
     if (s) return s;
     if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
@@ -380,6 +388,11 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int3
         const int64_t n0 = (int64_t)tokens * k;
         const int64_t tiles = (n0 + MFMA_BM - 1) / MFMA_BM + (n0 < E ? n0 : E);
         if (tiles > 65535) return QMOE_ERR_SHAPE;   // grid.y bound of the tiled kernels
+    }
+    if (phase_events) {
+        if (n_events < (x_dtype == QMOE_F32 ? 4 : 5)) return QMOE_ERR_SHAPE;
+        for (int i = 0; i < (x_dtype == QMOE_F32 ? 4 : 5); i++)
+            if (!phase_events[i]) return QMOE_ERR_NULL;
     }
     if (tokens == 0) return QMOE_OK;
     if (!x || !topk_ids || !topk_w || !out) return QMOE_ERR_NULL;
@@ -400,22 +413,32 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int3
     const LayerWs L = carve_layer(ws, E, H, F, tokens, k, x_dtype);
     const hipStream_t st = as_stream(stream);
     const QMat G = to_qmat(&desc->gate), U = to_qmat(&desc->up), D = to_qmat(&desc->down);
-    hipError_t e;
+    int phase = 0;
+    auto mark = [&]() -> hipError_t {
+        if (!phase_events) return hipSuccess;
+        return hipEventRecord(static_cast<hipEvent_t>(phase_events[phase++]), st);
+    };
+    hipError_t e = mark();
+    if (e != hipSuccess) return QMOE_ERR_HIP;
     if (x_dtype == QMOE_F32) {
         Worklist wl = L.wl;
         wl.tiles = nullptr;
         wl.n_tiles = nullptr;
         e = launch_decode_prep(topk_ids, (int)n, k, E, wl, static_cast<const float *>(x), tokens,
                                H, L.xd, out, st);
+        if (e == hipSuccess) e = mark();
         GemvRoute r{};
         r.wl = wl;
         r.topk_w = topk_w;
         r.k = k;
         r.max_active = L.max_active;
         if (e == hipSuccess) e = launch_gemv_gateup(G, U, L.xd, L.hd, r, st);
+        if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_gemv_down(D, L.hd, out, r, st);
+        if (e == hipSuccess) e = mark();
     } else {
         e = launch_worklist(topk_ids, (int)n, k, E, L.wl, L.hist, st);
+        if (e == hipSuccess) e = mark();
         MfmaRoute r{};
         r.wl = L.wl;
         r.topk_w = topk_w;
@@ -423,8 +446,11 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int3
         r.max_tiles = L.max_tiles;
         if (e == hipSuccess)
             e = launch_mfma_gateup(G, U, static_cast<const uint16_t *>(x), L.h16, r, st);
+        if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_mfma_down(D, L.h16, L.y, r, st);
+        if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_combine(L.y, L.wl.inv, tokens, k, H, out, st);
+        if (e == hipSuccess) e = mark();
     }
     return status_of(e);
 }

@@ -7,7 +7,7 @@
 // applied once per group inside the row loop (comments "blocked by GPU
 // driver instability" and the maintainer's data request, which asks for a
 // shift instead of a divide and the scale hoisted per group), and the fused
-// gate+up pair that reads x once for both matrices (Summary,
+// gate+up pair that loads the activation once for both matrices (Summary,
 // "matmul_i4_grouped_pair").
 //
 // MI355X mapping.  A row of I inputs is I/64 groups of 32 bytes; LPR lanes

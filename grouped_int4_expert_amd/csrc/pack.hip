@@ -3,7 +3,7 @@
 // Format (colibri pull request "cuda+engine: full fmt=4 (grouped int4 gs=64)
 // support", Summary: int4 rows are (I+1)/2 bytes, same nibble layout as the
 // per-row format; comment "implementation complete but system-instability":
-// the container holds unsigned offset nibbles 0..15): byte j of a row holds
+// the container keeps each code as a nibble 0..15 offset by 8): byte j of a row holds
 // element 2j in its low nibble and 2j+1 in its high nibble, each as q + 8.
 #include "common.h"
 #include "launch.h"

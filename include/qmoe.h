@@ -17,9 +17,10 @@
  *    library never allocates, frees or synchronises.  Work is enqueued on
  *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and the
  *    return value comes from host-side checks made before anything is
- *    enqueued.  A non-zero status means nothing was launched ("refuses
- *    rather than guessing": the fail-closed launcher guard of the same pull
- *    request, comment "implementation complete but system-instability").
+ *    enqueued.  A non-zero status means nothing was launched: like the
+ *    format guard of the same pull request (comment "implementation complete
+ *    but system-instability"), an unsupported input is declined up front
+ *    instead of being run with a guessed layout.
  *  - The library is stateless and thread-safe.  Concurrent calls on one
  *    stream serialise; calls on different streams that share a workspace
  *    race.
@@ -115,10 +116,9 @@ size_t qmoe_scale_count(int64_t rows, int64_t cols, int64_t group);
  * above: byte j of row o = (q[o][2j] + 8) & 15 | ((q[o][2j+1] + 8) & 15) << 4,
  * pad nibble 8 when cols is odd.  Codes outside [-8, 7] are stored wrapped
  * and, when n_bad != NULL, counted into *n_bad (a device int32 the call
- * zeroes first).  The offset encoding is the container's ("unsigned offset
- * encoding (0-15)", comment "implementation complete but
- * system-instability").  Requires cols even and packed 16-byte aligned rows
- * (cols % 32 == 0); q only 1-byte aligned. */
+ * zeroes first).  The offset encoding is the one the container uses (nibbles
+ * 0..15 standing for -8..7; comment "implementation complete but
+ * system-instability").  Any rows, cols >= 0; no alignment requirement. */
 int qmoe_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
               int32_t *n_bad, void *stream);
 
@@ -145,9 +145,9 @@ size_t qmoe_expert_ffn_workspace_bytes(const qmoe_qmat *gate,
 /* One expert: out[b] = down(silu(gate x_b) * (up x_b)), silu(z) =
  * z / (1 + exp(-z)).  gate/up are [F][H], down is [H][F] (expert 0 of each
  * descriptor).  x is f32 or bf16 [batch][H] per x_dtype; out is f32
- * [batch][H] and must not overlap x.  The fused pair reads x once for both
- * matrices (pull request Summary, "matmul_i4_grouped_pair: fused gate+up ...
- * reads x once instead of twice"). */
+ * [batch][H] and must not overlap x.  Gate and up are evaluated as one fused
+ * pair that loads each activation once for both matrices (pull request
+ * Summary, the matmul_i4_grouped_pair entry). */
 int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up,
                     const qmoe_qmat *down, int32_t x_dtype, const void *x,
                     int32_t batch, float *out, void *ws, size_t ws_bytes,
@@ -191,6 +191,20 @@ size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
 int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
                int32_t tokens, const int32_t *topk_ids, const float *topk_w,
                int32_t k, float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* qmoe_layer with phase markers: when phase_events is non-NULL it holds
+ * n_events hipEvent_t handles (passed as void*, created by the caller) and the
+ * call records events[0] before its first kernel and events[i] after phase i
+ * on `stream`.  Phases: f32 path 1 = worklist + activation digits, 2 = gate+up,
+ * 3 = down + combine (n_events >= 4); bf16 path 1 = worklist, 2 = gate+up,
+ * 3 = down, 4 = combine (n_events >= 5).  Fewer events = QMOE_ERR_SHAPE.
+ * Recording an event allocates nothing and does not synchronise.  This is
+ * the per-launch event timing the maintainer asks for in the pull request
+ * (data request: elapsed time around one launch per shape). */
+int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+                  int32_t tokens, const int32_t *topk_ids, const float *topk_w,
+                  int32_t k, float *out, void *ws, size_t ws_bytes, void *stream,
+                  void *const *phase_events, int32_t n_events);
 
 /* Byte offsets, inside a qmoe_layer workspace, of the worklist arrays the
  * call leaves behind (counts, offsets, pairs, inv, n_invalid). */

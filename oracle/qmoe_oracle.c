@@ -13,16 +13,16 @@
  * Sources (pages, by title and section):
  *  - colibri pull request "cuda+engine: full fmt=4 (grouped int4 gs=64)
  *    support + diagnostic harness":
- *      * Summary / Problem: one f32 scale per 64 consecutive input elements
- *        of a row instead of one per row; int4 rows are (I+1)/2 bytes, the
- *        same packed layout as the per-row int4 format.
+ *      * Summary / Problem: every row carries a separate f32 scale for each
+ *        run of 64 inputs (the older format had a single scale per row);
+ *        an int4 row occupies (I+1)/2 bytes, packed like the per-row format.
  *      * comment "implementation complete but system-instability": the
- *        on-disk container stores unsigned offset nibbles 0..15 and the GPU
+ *        on-disk container keeps nibbles as 0..15 with an offset and the GPU
  *        upload turns them into two's complement with a byte XOR of 0x88.
  *      * comment "blocked by GPU driver instability": the scale of element
  *        (o, i) is scales[o*ng + i/gs] with ng = ceil(I/gs); the CPU kernel
  *        accumulates per group and applies that group's scale; the fused
- *        gate+up pair reads x once for both matrices.
+ *        gate+up pair loads the activation a single time for both matrices.
  *      * maintainer comment "Here's the oracle you're missing": the
  *        reference is a plain dequant in double; the fused pair must equal
  *        two single passes element by element.
