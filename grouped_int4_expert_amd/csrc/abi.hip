@@ -80,8 +80,9 @@ struct LayerWs {
     Worklist wl;
     int32_t *hist;
     XDigits xd, hd;
-    uint16_t *h16;
-    float *y;
+    DecodePlan plan;
+    uint16_t *x16, *h16;
+    float *xinv, *y;
     int64_t bytes;
     int max_active, max_tiles;
     qmoe_layer_ws_view view;
@@ -105,11 +106,17 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
     L.wl.tile_m = MFMA_BM;
     L.hist = c.take<int32_t>(wl_scratch_ints(n, E));
     if (dtype == QMOE_F32) {
+        L.plan.rec = c.take<int32_t>(4 * (int64_t)L.max_active);
+        L.plan.tok = c.take<int32_t>(n);
+        L.plan.wsort = c.take<float>(n);
+        L.plan.max_active = L.max_active;
         L.xd.dig = c.take<uint32_t>((int64_t)T * (H / 32) * 20);
         L.xd.fac = c.take<float>((int64_t)T * (H / 32));
         L.hd.dig = c.take<uint32_t>(n * (F / 32) * 20);
         L.hd.fac = c.take<float>(n * (F / 32));
     } else {
+        L.x16 = c.take<uint16_t>((int64_t)T * H);
+        L.xinv = c.take<float>(T);
         L.h16 = c.take<uint16_t>(n * F);
         L.y = c.take<float>(n * H);
     }
@@ -245,6 +252,8 @@ size_t qmoe_expert_ffn_workspace_bytes(const qmoe_qmat *gate, const qmoe_qmat *u
         c.take<uint32_t>(batch * (F / 32) * 20);
         c.take<float>(batch * (F / 32));
     } else {
+        c.take<uint16_t>(batch * H);
+        c.take<float>(batch);
         c.take<uint16_t>(batch * F);
     }
     return (size_t)c.off;
@@ -266,7 +275,7 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
     if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
         return QMOE_ERR_UNSUPPORTED;
-    if (x_dtype == QMOE_BF16 && H % 128 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype == QMOE_BF16 && H % 64 != 0) return QMOE_ERR_UNSUPPORTED;
     if (batch == 0) return QMOE_OK;
     if (!x || !out) return QMOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(out)) return QMOE_ERR_ALIGN;
@@ -287,20 +296,22 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
         hd.dig = c.take<uint32_t>((int64_t)batch * (F / 32) * 20);
         hd.fac = c.take<float>((int64_t)batch * (F / 32));
         GemvRoute r{};
-        r.wl.pairs = nullptr;
         r.ntok = batch;
-        r.k = 1;
+        r.batch_tokens = batch;
         e = launch_xdigits(static_cast<const float *>(x), batch, H, xd, st);
         if (e == hipSuccess) e = launch_gemv_gateup(to_qmat(gate), to_qmat(up), xd, hd, r, st);
         if (e == hipSuccess) e = launch_gemv_down(to_qmat(down), hd, out, r, st);
     } else {
+        uint16_t *x16 = c.take<uint16_t>((int64_t)batch * H);
+        float *xinv = c.take<float>(batch);
         uint16_t *h16 = c.take<uint16_t>((int64_t)batch * F);
         MfmaRoute r{};
         r.wl.pairs = nullptr;
         r.ntok = batch;
         r.k = 1;
-        e = launch_mfma_gateup(to_qmat(gate), to_qmat(up), static_cast<const uint16_t *>(x), h16,
-                               r, st);
+        e = launch_xprep(static_cast<const uint16_t *>(x), batch, H, x16, xinv, st);
+        if (e == hipSuccess)
+            e = launch_mfma_gateup(to_qmat(gate), to_qmat(up), x16, xinv, h16, r, st);
         if (e == hipSuccess) e = launch_mfma_down(to_qmat(down), h16, out, r, st);
     }
     return status_of(e);
@@ -383,7 +394,7 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
     const int E = desc->experts, H = desc->hidden, F = desc->inter;
     if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
         return QMOE_ERR_UNSUPPORTED;
-    if (x_dtype == QMOE_BF16 && H % 128 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype == QMOE_BF16 && H % 64 != 0) return QMOE_ERR_UNSUPPORTED;
     {
         const int64_t n0 = (int64_t)tokens * k;
         const int64_t tiles = (n0 + MFMA_BM - 1) / MFMA_BM + (n0 < E ? n0 : E);
@@ -424,28 +435,30 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         Worklist wl = L.wl;
         wl.tiles = nullptr;
         wl.n_tiles = nullptr;
-        e = launch_decode_prep(topk_ids, (int)n, k, E, wl, static_cast<const float *>(x), tokens,
-                               H, L.xd, out, st);
+        e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, L.plan,
+                               static_cast<const float *>(x), tokens, H, L.xd, out, st);
         if (e == hipSuccess) e = mark();
         GemvRoute r{};
-        r.wl = wl;
-        r.topk_w = topk_w;
-        r.k = k;
+        r.rec = L.plan.rec;
+        r.tok = L.plan.tok;
+        r.wsort = L.plan.wsort;
         r.max_active = L.max_active;
+        r.batch_tokens = tokens;
         if (e == hipSuccess) e = launch_gemv_gateup(G, U, L.xd, L.hd, r, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_gemv_down(D, L.hd, out, r, st);
         if (e == hipSuccess) e = mark();
     } else {
         e = launch_worklist(topk_ids, (int)n, k, E, L.wl, L.hist, st);
+        if (e == hipSuccess)
+            e = launch_xprep(static_cast<const uint16_t *>(x), tokens, H, L.x16, L.xinv, st);
         if (e == hipSuccess) e = mark();
         MfmaRoute r{};
         r.wl = L.wl;
         r.topk_w = topk_w;
         r.k = k;
         r.max_tiles = L.max_tiles;
-        if (e == hipSuccess)
-            e = launch_mfma_gateup(G, U, static_cast<const uint16_t *>(x), L.h16, r, st);
+        if (e == hipSuccess) e = launch_mfma_gateup(G, U, L.x16, L.xinv, L.h16, r, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_mfma_down(D, L.h16, L.y, r, st);
         if (e == hipSuccess) e = mark();

@@ -131,22 +131,86 @@ __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XR
 // Expert and sorted-position range of this block.
 __device__ __forceinline__ bool block_expert(const GemvRoute &r, int a, int &e, int &p0,
                                              int &p1) {
-    if (r.wl.pairs == nullptr) {
+    if (r.rec == nullptr) {
         if (a != 0) return false;
         e = 0;
         p0 = 0;
         p1 = r.ntok;
         return true;
     }
-    if (a >= r.wl.n_active[0]) return false;
-    e = r.wl.active[a];
-    p0 = r.wl.offsets[e];
-    p1 = r.wl.offsets[e + 1];
+    const u32x4 rc = *(const u32x4 *)(r.rec + 4 * a);
+    e = (int)rc.x;
+    if (e < 0) return false;
+    p0 = (int)rc.y;
+    p1 = (int)rc.z;
     return true;
 }
 
 __device__ __forceinline__ int64_t token_of(const GemvRoute &r, int pos) {
-    return r.wl.pairs == nullptr ? pos : r.wl.pairs[pos] / r.k;
+    return r.rec == nullptr ? pos : r.tok[pos];
+}
+
+// Sum over groups of LPR consecutive lanes with DPP row shifts and row
+// broadcasts (VALU only); the sum is valid in the last lane of each group.
+__device__ __forceinline__ float dpp_add(float v, int t) { return v + __int_as_float(t); }
+template <int LPR>
+__device__ __forceinline__ float reduce_dpp(float v) {
+    const int vi = 0;
+    (void)vi;
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    if (LPR >= 16)
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    if (LPR >= 32)   // row_bcast:15 into rows 1 and 3
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    if (LPR >= 64)   // row_bcast:31 into rows 2 and 3
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+// Rows per batch: about 128 bytes of weights in flight per lane per batch.
+template <int GPL, int NSTEP>
+constexpr int batch_rows() {
+    return (4 / GPL) < NSTEP ? (4 / GPL < 1 ? 1 : 4 / GPL) : NSTEP;
+}
+
+// Stream NSTEP rows per lane group (LPR lanes) in batches of U rows, the
+// next batch's loads issued before the current batch is computed.
+// row_at(step, q, s) gives the packed row and its scales (q == nullptr:
+// no row); emit(step, j, value) runs on the last lane of the group.
+template <int GPL, int LPR, int TB, int U, int NSTEP, class RowAt, class Prologue, class Emit>
+__device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int ng, int lr,
+                                            RowAt row_at, Prologue prologue, Emit emit) {
+    constexpr int NB = NSTEP / U;
+    static_assert(NB * U == NSTEP, "NSTEP must be a multiple of U");
+    WReg<GPL, U> w[2];
+    auto load_batch = [&](int b, WReg<GPL, U> &dst) {
+        const uint8_t *rq[U];
+        const float *rs[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) row_at(b * U + u, rq[u], rs[u]);
+        load_rows<GPL, LPR, U>(dst, rq, rs, ng, lr);
+    };
+    // The first weight batch depends only on the expert; issue it before the
+    // prologue's dependent chain (pair -> token -> activation digits).
+    load_batch(0, w[0]);
+    prologue();
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        if (b + 1 < NB) load_batch(b + 1, w[(b + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < TB; j++) {
+            if (j < nt) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    float v = row_dot<GPL, U>(w[b & 1], u, xr[j]);
+                    v = reduce_dpp<LPR>(v);
+                    if (lr == LPR - 1) emit(b * U + u, j, v);
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -157,10 +221,10 @@ __device__ __forceinline__ int64_t token_of(const GemvRoute &r, int pos) {
 template <int GPL, int LPR, int TB>
 __global__ void __launch_bounds__(GV_THREADS) gemv_gateup_kernel(QMat G, QMat Up, XDigits xd,
                                                                  XDigits hd, GemvRoute r) {
-    constexpr int RS = GV_THREADS / LPR;       // row slots per block
+    constexpr int RS = GV_THREADS / LPR;       // lane groups per block
     constexpr int NR = 64;                     // row tasks per block
-    constexpr int RPS = NR / RS;               // rows per slot
-    constexpr int U = RPS < 4 ? RPS : 4;
+    constexpr int NSTEP = NR / RS;             // rows per lane group
+    constexpr int U = batch_rows<GPL, NSTEP>();
     __shared__ float res[TB][NR];
 
     int e, p0, p1;
@@ -174,38 +238,24 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_gateup_kernel(QMat G, QMat Up
     const uint8_t *uq = Up.q + (int64_t)e * Up.q_stride;
     const float *gs = G.s + (int64_t)e * G.s_stride;
     const float *us = Up.s + (int64_t)e * Up.s_stride;
+    auto row_at = [&](int step, const uint8_t *&q, const float *&s) {
+        const int ri = slot * NSTEP + step;       // 0..63: gate rows, then up rows
+        const int o = row0 + (ri & 31);
+        q = (ri < 32 ? gq : uq) + (int64_t)o * rb;
+        s = (ri < 32 ? gs : us) + (int64_t)o * ng;
+    };
 
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
         XReg<GPL> xr[TB];
+        stream_rows<GPL, LPR, TB, U, NSTEP>(
+            xr, nt, ng, lr, row_at,
+            [&]() {
 #pragma unroll
-        for (int j = 0; j < TB; j++)
-            if (j < nt) load_digits<GPL, LPR>(xr[j], xd, token_of(r, t0 + j), ncx, ng, lr);
-
-        for (int rb0 = 0; rb0 < RPS; rb0 += U) {
-            const uint8_t *rowq[U];
-            const float *rows[U];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int ri = slot * RPS + rb0 + u;          // 0..63
-                const int o = row0 + (ri & 31);
-                rowq[u] = (ri < 32 ? gq : uq) + (int64_t)o * rb;
-                rows[u] = (ri < 32 ? gs : us) + (int64_t)o * ng;
-            }
-            WReg<GPL, U> wr;
-            load_rows<GPL, LPR, U>(wr, rowq, rows, ng, lr);
-#pragma unroll
-            for (int j = 0; j < TB; j++) {
-                if (j < nt) {
-#pragma unroll
-                    for (int u = 0; u < U; u++) {
-                        float v = row_dot<GPL, U>(wr, u, xr[j]);
-                        v = group_sum<LPR>(v);
-                        if (lr == 0) res[j][slot * RPS + rb0 + u] = v;
-                    }
-                }
-            }
-        }
+                for (int j = 0; j < TB; j++)
+                    if (j < nt) load_digits<GPL, LPR>(xr[j], xd, token_of(r, t0 + j), ncx, ng, lr);
+            },
+            [&](int step, int j, float v) { res[j][slot * NSTEP + step] = v; });
         __syncthreads();
         // epilogue: wave j quantises token j's 32 values of h
         const int w = wave_id(), lane = lane_id();
@@ -233,67 +283,56 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_down_kernel(QMat D, XDigits h
                                                                GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;
     constexpr int NR = 64;
-    constexpr int RPS = NR / RS;
-    constexpr int U = RPS < 4 ? RPS : 4;
+    constexpr int NSTEP = NR / RS;
+    constexpr int U = batch_rows<GPL, NSTEP>();
 
     int e, p0, p1;
     if (!block_expert(r, blockIdx.y, e, p0, p1)) return;
     const int O = D.rows, I = D.cols;
     const int ng = I / 64, ncx = I / XD_CHUNK;
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
-    const int row0 = blockIdx.x * NR;
+    const int row0 = blockIdx.x * NR + slot * NSTEP;
     const int64_t rbytes = I / 2;
     const uint8_t *dq = D.q + (int64_t)e * D.q_stride;
     const float *ds = D.s + (int64_t)e * D.s_stride;
-    const bool routed = r.wl.pairs != nullptr;
+    const bool routed = r.rec != nullptr;
+    auto row_at = [&](int step, const uint8_t *&q, const float *&s) {
+        const int o = row0 + step;
+        q = o < O ? dq + (int64_t)o * rbytes : nullptr;
+        s = ds + (int64_t)(o < O ? o : 0) * ng;
+    };
 
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
         XReg<GPL> xr[TB];
         float wj[TB];
         int64_t tj[TB];
-#pragma unroll
-        for (int j = 0; j < TB; j++) {
-            if (j < nt) {
-                load_digits<GPL, LPR>(xr[j], hd, t0 + j, ncx, ng, lr);
-                if (routed) {
-                    const int p = r.wl.pairs[t0 + j];
-                    tj[j] = p / r.k;
-                    wj[j] = r.topk_w[p];
-                } else {
-                    tj[j] = t0 + j;
-                    wj[j] = 1.f;
-                }
-            }
-        }
-        for (int rb0 = 0; rb0 < RPS; rb0 += U) {
-            const uint8_t *rowq[U];
-            const float *rows[U];
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int o = row0 + slot * RPS + rb0 + u;
-                rowq[u] = o < O ? dq + (int64_t)o * rbytes : nullptr;
-                rows[u] = ds + (int64_t)(o < O ? o : 0) * ng;
-            }
-            WReg<GPL, U> wr;
-            load_rows<GPL, LPR, U>(wr, rowq, rows, ng, lr);
+        auto prologue = [&]() {
 #pragma unroll
             for (int j = 0; j < TB; j++) {
+                wj[j] = 0.f;
+                tj[j] = 0;
                 if (j < nt) {
-#pragma unroll
-                    for (int u = 0; u < U; u++) {
-                        float v = row_dot<GPL, U>(wr, u, xr[j]);
-                        v = group_sum<LPR>(v);
-                        const int o = row0 + slot * RPS + rb0 + u;
-                        if (lr == 0 && o < O) {
-                            float *dst = out + tj[j] * O + o;
-                            if (routed) unsafeAtomicAdd(dst, wj[j] * v);
-                            else *dst = v;
-                        }
+                    load_digits<GPL, LPR>(xr[j], hd, t0 + j, ncx, ng, lr);
+                    if (routed) {
+                        tj[j] = r.tok[t0 + j];
+                        wj[j] = r.wsort[t0 + j];
+                    } else {
+                        tj[j] = t0 + j;
+                        wj[j] = 1.f;
                     }
                 }
             }
-        }
+        };
+        stream_rows<GPL, LPR, TB, U, NSTEP>(xr, nt, ng, lr, row_at, prologue,
+                                            [&](int step, int j, float v) {
+                                                const int o = row0 + step;
+                                                if (o < O) {
+                                                    float *dst = out + tj[j] * O + o;
+                                                    if (routed) unsafeAtomicAdd(dst, wj[j] * v);
+                                                    else *dst = v;
+                                                }
+                                            });
     }
 }
 
@@ -302,10 +341,27 @@ struct GemvShape {
     int gpl, lpr;
 };
 
+// Fewer groups per lane is preferred: one group per lane keeps two tokens'
+// digits in registers (a second token costs no second weight pass), so it
+// wins whenever at least 70% of the lanes have a group.
 static GemvShape choose_shape(int ng) {
+    const int lprs[4] = {64, 32, 16, 8};
+    for (int gpl = 1; gpl <= 3; gpl++) {
+        GemvShape best{0, 0};
+        double best_eff = 0;
+        for (int li = 0; li < 4; li++) {
+            const int lpr = lprs[li];
+            if (gpl * lpr < ng || (gpl - 1) * lpr >= ng) continue;
+            const double eff = (double)ng / (gpl * lpr);
+            if (eff > best_eff + 1e-9) {
+                best_eff = eff;
+                best = GemvShape{gpl, lpr};
+            }
+        }
+        if (best.gpl && best_eff >= 0.7) return best;
+    }
     GemvShape best{0, 0};
     double best_eff = 0;
-    const int lprs[4] = {64, 32, 16, 8};
     for (int gpl = 1; gpl <= 3; gpl++)
         for (int li = 0; li < 4; li++) {
             const int lpr = lprs[li];
@@ -324,22 +380,32 @@ bool gemv_supported(int cols) {
     return choose_shape(cols / 64).gpl != 0;
 }
 
-#define QMOE_GEMV_SHAPES(X) \
-    X(1, 64) X(1, 32) X(1, 16) X(1, 8) X(2, 64) X(2, 32) X(2, 16) X(2, 8) X(3, 64) X(3, 32) \
-        X(3, 16) X(3, 8)
+// (groups per lane, lanes per row, tokens per pass).  Two tokens per pass
+// only with one group per lane (register budget).
+#define QMOE_GEMV_SHAPES(X)                                                                     \
+    X(1, 64, 1) X(1, 32, 1) X(1, 16, 1) X(1, 8, 1) X(1, 64, 2) X(1, 32, 2) X(1, 16, 2) X(1, 8, 2) \
+        X(2, 64, 1) X(2, 32, 1) X(2, 16, 1) X(2, 8, 1) X(3, 64, 1) X(3, 32, 1) X(3, 16, 1)      \
+            X(3, 8, 1)
 
-template <int GPL>
-constexpr int tb_for() { return GPL == 1 ? 2 : 1; }
+// Tokens per weight pass (measured on MI355X): gate+up keeps two tokens'
+// digits in registers once the batch has more than one token; the down
+// projection runs faster with one token per pass at every batch size (fewer
+// registers, more waves in flight; its extra passes hit in L2).
+static int tokens_per_pass(const GemvShape &s, const GemvRoute &r, bool gateup) {
+    if (s.gpl != 1 || !gateup) return 1;
+    return r.batch_tokens > 1 ? 2 : 1;
+}
 
 hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDigits hd,
                               const GemvRoute &r, hipStream_t st) {
     const GemvShape s = choose_shape(gate.cols / 64);
-    const dim3 grid(gate.rows / 32, r.wl.pairs ? r.max_active : 1);
-#define X(G_, L_)                                                                             \
-    if (s.gpl == G_ && s.lpr == L_) {                                                         \
-        hipLaunchKernelGGL((gemv_gateup_kernel<G_, L_, tb_for<G_>()>), grid, dim3(GV_THREADS), \
-                           0, st, gate, up, xd, hd, r);                                       \
-        return hipGetLastError();                                                             \
+    const int tb = tokens_per_pass(s, r, true);
+    const dim3 grid(gate.rows / 32, r.rec ? r.max_active : 1);
+#define X(G_, L_, T_)                                                                      \
+    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                          \
+        hipLaunchKernelGGL((gemv_gateup_kernel<G_, L_, T_>), grid, dim3(GV_THREADS), 0, st, \
+                           gate, up, xd, hd, r);                                           \
+        return hipGetLastError();                                                          \
     }
     QMOE_GEMV_SHAPES(X)
 #undef X
@@ -349,12 +415,13 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
 hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const GemvRoute &r,
                             hipStream_t st) {
     const GemvShape s = choose_shape(down.cols / 64);
-    const dim3 grid((down.rows + 63) / 64, r.wl.pairs ? r.max_active : 1);
-#define X(G_, L_)                                                                              \
-    if (s.gpl == G_ && s.lpr == L_) {                                                          \
-        hipLaunchKernelGGL((gemv_down_kernel<G_, L_, tb_for<G_>()>), grid, dim3(GV_THREADS), 0, \
-                           st, down, hd, out, r);                                              \
-        return hipGetLastError();                                                              \
+    const int tb = tokens_per_pass(s, r, false);
+    const dim3 grid((down.rows + 63) / 64, r.rec ? r.max_active : 1);
+#define X(G_, L_, T_)                                                                    \
+    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                        \
+        hipLaunchKernelGGL((gemv_down_kernel<G_, L_, T_>), grid, dim3(GV_THREADS), 0, st, \
+                           down, hd, out, r);                                            \
+        return hipGetLastError();                                                        \
     }
     QMOE_GEMV_SHAPES(X)
 #undef X
@@ -363,9 +430,8 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
 
 hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y, hipStream_t st) {
     GemvRoute r{};
-    r.wl.pairs = nullptr;
     r.ntok = batch;
-    r.k = 1;
+    r.batch_tokens = batch;
     return launch_gemv_down(w, xd, y, r, st);
 }
 

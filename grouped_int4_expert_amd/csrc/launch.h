@@ -47,11 +47,23 @@ int64_t wl_scratch_ints(int64_t n, int E);
 hipError_t launch_worklist(const int32_t *ids, int n, int k, int E, const Worklist &wl,
                            int32_t *scratch, hipStream_t st);
 
-// Decode preparation in one launch: the worklist (block 0), x -> digits for
-// all tokens, and out <- 0.
-hipError_t launch_decode_prep(const int32_t *ids, int n, int k, int E, const Worklist &wl,
-                              const float *x, int tokens, int hidden, XDigits xd, float *out,
-                              hipStream_t st);
+// Per-call plan of the decode GEMVs, written by the preparation kernel so a
+// GEMV block starts with one load: rec[4a..4a+3] = (expert, first and end
+// sorted position, 0) for active slot a (expert -1 past the last active
+// slot, up to max_active); tok/wsort = token and routing weight of each
+// sorted position.
+struct DecodePlan {
+    int32_t *rec;       // [4 * max_active]
+    int32_t *tok;       // [n]
+    float *wsort;       // [n]
+    int max_active;
+};
+
+// Decode preparation in one launch: the worklist and plan (block 0), x ->
+// digits for all tokens, and out <- 0.
+hipError_t launch_decode_prep(const int32_t *ids, const float *topk_w, int n, int k, int E,
+                              const Worklist &wl, const DecodePlan &plan, const float *x,
+                              int tokens, int hidden, XDigits xd, float *out, hipStream_t st);
 
 // x -> digits only (matvec and the single-expert FFN).
 hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStream_t st);
@@ -60,11 +72,12 @@ hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStr
 // offsets[e]..offsets[e+1]; in "direct" mode (wl.pairs == nullptr) there is
 // one expert (0) with positions 0..ntok-1 = tokens 0..ntok-1, weight 1.
 struct GemvRoute {
-    Worklist wl;
-    const float *topk_w;   // [n] routing weights (down, routed mode)
-    int k;                 // top-k (pair -> token)
+    const int32_t *rec;    // plan records (nullptr: direct mode)
+    const int32_t *tok;    // token of each sorted position
+    const float *wsort;    // routing weight of each sorted position
     int max_active;        // grid bound on active experts
     int ntok;              // direct mode: tokens
+    int batch_tokens;      // tokens in the call (a launch-shape hint)
 };
 
 // h digits for the down projection: silu(gate x) * (up x) per sorted pair.
@@ -86,9 +99,13 @@ struct MfmaRoute {
     int max_tiles;     // grid bound on tiles
     int ntok;          // direct mode
 };
+// x bf16 [tokens][hidden] -> x16 f16 scaled by 2^k_t (octet-permuted), xinv = 2^-k_t.
+hipError_t launch_xprep(const uint16_t *x, int tokens, int hidden, uint16_t *x16, float *xinv,
+                        hipStream_t st);
 // h16[pos][F] = silu(G x) * (U x) as f16, pos = sorted pair position.
-hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *x_bf16,
-                              uint16_t *h16, const MfmaRoute &r, hipStream_t st);
+hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *x16,
+                              const float *xinv, uint16_t *h16, const MfmaRoute &r,
+                              hipStream_t st);
 // Y[pos][H] = w * (D h) in f32 (direct mode: out[t] = D h).
 hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y,
                             const MfmaRoute &r, hipStream_t st);

@@ -239,14 +239,112 @@ hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStr
     return hipGetLastError();
 }
 
+// Inclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < QMOE_WAVE; o <<= 1) {
+        const int y = __shfl_up(x, o, QMOE_WAVE);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// The same worklist built by one wave, for small pair counts: no block
+// barriers, only the in-order LDS traffic of a single wave.
+__device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int n,
+                        int k, int E, const Worklist &wl, const DecodePlan &plan,
+                        int *cnt /* [E+1] */, int *run /* [E+1] */) {
+    const int lane = lane_id();
+    for (int e = lane; e <= E; e += QMOE_WAVE) cnt[e] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    for (int p = lane; p < n; p += QMOE_WAVE) {
+        int e = ids[p];
+        if (e < 0 || e >= E) e = E;
+        atomicAdd(&cnt[e], 1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    int carry = 0, acarry = 0;
+    for (int base = 0; base < E; base += QMOE_WAVE) {
+        const int e = base + lane;
+        const int c = e < E ? cnt[e] : 0;
+        const int inc = wave_inclusive_scan(c);
+        const int off = carry + inc - c;
+        const int a = c > 0 ? 1 : 0;
+        const int ainc = wave_inclusive_scan(a);
+        if (e < E) {
+            wl.counts[e] = c;
+            wl.offsets[e] = off;
+            run[e] = off;
+            if (a && wl.active) wl.active[acarry + ainc - 1] = e;
+            if (a && plan.rec) {
+                int32_t *rc = plan.rec + 4 * (acarry + ainc - 1);
+                rc[0] = e;
+                rc[1] = off;
+                rc[2] = off + c;
+                rc[3] = 0;
+            }
+        }
+        carry += __shfl(inc, QMOE_WAVE - 1, QMOE_WAVE);
+        acarry += __shfl(ainc, QMOE_WAVE - 1, QMOE_WAVE);
+    }
+    if (lane == 0) {
+        wl.offsets[E] = carry;
+        wl.n_invalid[0] = cnt[E];
+        run[E] = carry;
+        if (wl.n_active) wl.n_active[0] = acarry;
+    }
+    if (plan.rec)
+        for (int a = acarry + lane; a < plan.max_active; a += QMOE_WAVE) plan.rec[4 * a] = -1;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    int nbits = 1;
+    while ((1 << nbits) <= E) nbits++;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = 0; base < n; base += QMOE_WAVE) {
+        const int p = base + lane;
+        const bool act = p < n;
+        int e = E;
+        if (act) {
+            e = ids[p];
+            if (e < 0 || e >= E) e = E;
+        }
+        uint64_t m = __ballot(act);
+        for (int bit = 0; bit < nbits; bit++) {
+            const bool set = (e >> bit) & 1;
+            const uint64_t bb = __ballot(set);
+            m &= set ? bb : ~bb;
+        }
+        const int rank = __popcll(m & below);
+        const int cnt_e = __popcll(m);
+        if (act) {
+            const int pos = run[e] + rank;
+            wl.pairs[pos] = e < E ? p : -1;
+            wl.inv[p] = e < E ? pos : -1;
+            if (e < E && plan.tok) {
+                plan.tok[pos] = p / k;
+                plan.wsort[pos] = topk_w[p];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        if (act && rank == 0) run[e] += cnt_e;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // Block 0 builds the worklist; the other blocks turn x into digits and clear
 // out (the down projection accumulates into it).
 __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
-    const int32_t *__restrict__ ids, int n, int E, Worklist wl, const float *__restrict__ x,
-    int tokens, int hidden, XDigits xd, float *__restrict__ out) {
+    const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int n, int k, int E,
+    Worklist wl, DecodePlan plan, const float *__restrict__ x, int tokens, int hidden, XDigits xd,
+    float *__restrict__ out) {
     if (blockIdx.x == 0) {
-        __shared__ WlShared sh;
-        wl_block(ids, n, E, wl, nullptr, 1, 0, sh);
+        __shared__ int cnt[WL_MAX_E + 1], run[WL_MAX_E + 1];
+        if (wave_id() == 0) wl_wave(ids, topk_w, n, k, E, wl, plan, cnt, run);
         return;
     }
     const int64_t hpb = blockDim.x / 32;
@@ -259,16 +357,15 @@ __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
         out[i] = 0.0f;
 }
 
-hipError_t launch_decode_prep(const int32_t *ids, int n, int k, int E, const Worklist &wl,
-                              const float *x, int tokens, int hidden, XDigits xd, float *out,
-                              hipStream_t st) {
-    (void)k;
+hipError_t launch_decode_prep(const int32_t *ids, const float *topk_w, int n, int k, int E,
+                              const Worklist &wl, const DecodePlan &plan, const float *x,
+                              int tokens, int hidden, XDigits xd, float *out, hipStream_t st) {
     const int64_t nchunks = (int64_t)tokens * (hidden / XD_CHUNK);
     int64_t g = (nchunks + 31) / 32;     // 32 half-waves per 1024-thread block
     if (g < 1) g = 1;
     if (g > 1024) g = 1024;
-    hipLaunchKernelGGL(decode_prep_kernel, dim3((int)g + 1), dim3(WL_THREADS), 0, st, ids, n,
-                       E, wl, x, tokens, hidden, xd, out);
+    hipLaunchKernelGGL(decode_prep_kernel, dim3((int)g + 1), dim3(WL_THREADS), 0, st, ids,
+                       topk_w, n, k, E, wl, plan, x, tokens, hidden, xd, out);
     return hipGetLastError();
 }
 

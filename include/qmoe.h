@@ -196,8 +196,8 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
  * n_events hipEvent_t handles (passed as void*, created by the caller) and the
  * call records events[0] before its first kernel and events[i] after phase i
  * on `stream`.  Phases: f32 path 1 = worklist + activation digits, 2 = gate+up,
- * 3 = down + combine (n_events >= 4); bf16 path 1 = worklist, 2 = gate+up,
- * 3 = down, 4 = combine (n_events >= 5).  Fewer events = QMOE_ERR_SHAPE.
+ * 3 = down + combine (n_events >= 4); bf16 path 1 = worklist + activation
+ * prep, 2 = gate+up, 3 = down, 4 = combine (n_events >= 5).  Fewer events = QMOE_ERR_SHAPE.
  * Recording an event allocates nothing and does not synchronise.  This is
  * the per-launch event timing the maintainer asks for in the pull request
  * (data request: elapsed time around one launch per shape). */

@@ -236,3 +236,93 @@ def test_layer_worklist_left_in_workspace():
         ref = orc().worklist(ids.numpy(), 16)
         for key in ("counts", "offsets", "pairs", "inv"):
             assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+
+
+# ------------------------------------------- large skewed layer (Zipf) ---
+
+@pytest.mark.parametrize("dtype,T,toks", [("f32", 64, [0, 13, 40, 63]),
+                                          ("bf16", 2048, [0, 511, 1024, 2047])])
+def test_layer_e256_zipf(dtype, T, toks):
+    say(f"zipf layer E=256 H=6144 F=2048 T={T} {dtype}")
+    L = _big_layer(256, 6144, 2048, 4)
+    out, ref = _layer_case(L, T, 8, dtype, logits="zipf", seed=40 + T, tokens=toks)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+# ------------------------------------------------------------ edge cases ---
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_single_expert_k1_equals_expert_ffn(dtype):
+    """E = 1, k = 1, weight 1: the layer is the expert FFN (GPU vs GPU, both
+    also within tolerance of the oracle)."""
+    say(f"layer E=1 k=1 {dtype}")
+    L = Layer(1, 256, 128, seed=31)
+    g = synth.generator(77)
+    x = synth.rand_x(g, (70, 256))
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    ids = torch.zeros(70, 1, dtype=torch.int32)
+    w = torch.ones(70, 1)
+    lay = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ffn = qm.qmoe_expert_ffn(L.packed["qg"][0], L.s_dev["sg"][0], L.packed["qu"][0],
+                             L.s_dev["su"][0], L.packed["qd"][0], L.s_dev["sd"][0], 256, 128,
+                             x.to(DEV)).cpu().numpy()
+    ref = L.oracle_layer(x, ids, w)
+    tol = F32_TOL if dtype == "f32" else BF16_TOL
+    assert rel_l2(lay, ref) <= tol and rel_l2(ffn, ref) <= tol
+    assert rel_l2(lay, ffn) <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_all_ids_invalid_gives_zero(dtype):
+    say(f"layer all ids invalid {dtype}")
+    L = Layer(4, 256, 128, seed=32)
+    x = synth.rand_x(synth.generator(5), (6, 256))
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    ids = torch.tensor([[-1, 4]] * 6, dtype=torch.int32)
+    w = torch.ones(6, 2)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV))
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_layer_wide_topk():
+    """k = 16 of 32 experts, f32 and bf16."""
+    L = Layer(32, 256, 128, seed=33)
+    for dtype in ("f32", "bf16"):
+        say(f"layer k=16 {dtype}")
+        out, ref = _layer_case(L, 20, 16, dtype, seed=16)
+        assert rel_l2(out, ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_graph_replays_match_eager(dtype):
+    """Capture qmoe_layer in a HIP graph and replay it several times with
+    eager work and synchronisation in between; every replay must match the
+    eager result (the library records no memset nodes)."""
+    say(f"layer graph replay {dtype}")
+    L = Layer(16, 256, 128, seed=34)
+    g = synth.generator(3)
+    wl = synth.Workload("t", 16, 256, 128, 4, 33, dtype, "normal", 3)
+    x, ids, w = synth.layer_inputs(wl, g)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), w.to(DEV)
+    code = qm.QMOE_F32 if dtype == "f32" else qm.QMOE_BF16
+    ws = torch.empty(L.dev.workspace_bytes(33, 4, code), dtype=torch.uint8, device=DEV)
+    out = torch.empty(33, 256, device=DEV)
+    qm.qmoe_layer(L.dev, xd, idd, wd, out=out, ws=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=s):
+        qm.qmoe_layer(L.dev, xd, idd, wd, out=out, ws=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)                 # stale workspace must not matter
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        assert rel_l2(out.cpu().numpy(), eager.cpu().numpy()) <= 1e-6, rep
