@@ -153,6 +153,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="time only part of the step (for counter runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy three times and exit "
+                         "(reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -168,6 +173,14 @@ def main():
     qm.load()
     dev = "cuda"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": a.numel() * 4}))
+        return
 
     # ---------------- inputs, resident in HBM before timing ----------------
     log("generating weights ...")
@@ -262,7 +275,13 @@ def main():
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        graph.replay()
+        if args.only != "prefill":
+            graph.replay()
+        if args.only == "decode":
+            if evs is not None:
+                for ev in evs[1:]:
+                    ev.record()
+            return
         if evs is not None:
             qm.qmoe_layer_ex(pre_layer, xp_d, ip_d, wp_d, evs[1:], out=out_p, ws=ws_p)
         else:

@@ -40,6 +40,12 @@ constexpr int BM = MFMA_BM;   // 128 token rows per tile
 // LDS offset (in 16-bit elements) of octet `o` of row `m` in a 128 x 64 tile.
 __device__ __forceinline__ int sw_off(int m, int o) { return m * 64 + ((o ^ (m & 7)) << 3); }
 
+// s_waitcnt immediate (gfx9 layout) that waits until at most n vector memory
+// loads of this wave are outstanding and leaves the other counters alone.
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Position of element e (0..7) of an octet after the unpack permutation.
 __device__ __forceinline__ int octet_pos(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
 
@@ -79,6 +85,26 @@ __device__ __forceinline__ bool tile_info(const MfmaRoute &r, int tile, TileInfo
     ti.rows = min(BM, c - ti.row0);
     return true;
 }
+
+// Work item (tile, column block) of this block.  The GPU hands linear block
+// ids to its 8 XCDs round-robin, and each XCD has its own L2; so each XCD is
+// given one contiguous run of the real items (their count comes from the
+// device worklist), column blocks of a tile adjacent: a tile's activation
+// rows and an expert's weight slices are then fetched into one L2 instead of
+// up to eight.  gridDim.x is a multiple of 8 and >= the largest item count.
+__device__ __forceinline__ bool work_item(const MfmaRoute &r, int ncb, int &tile, int &cb) {
+    const int ntiles = r.wl.pairs ? r.wl.n_tiles[0] : (r.ntok + BM - 1) / BM;
+    const int W = ntiles * ncb;
+    const int per_xcd = (W + 7) / 8;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    const int w = xcd * per_xcd + local;
+    if (local >= per_xcd || w >= W) return false;
+    tile = w / ncb;
+    cb = w - tile * ncb;
+    return true;
+}
+
+static unsigned xcd_grid(int64_t items) { return (unsigned)(((items + 7) / 8) * 8); }
 
 // ---------------------------------------------------------------------------
 // Activation prep: x bf16 [T][H] -> x16 f16 (scaled by 2^k_t, octet-permuted)
@@ -130,23 +156,39 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Shared main loop.  The block owns a 128-row tile of f16 activation rows
-// (arow[i]: row pointers of the 4 pieces this thread stages) and each wave
-// NF 32-column weight fragments (brow/srow per fragment).  acc[i][j]: m-frag i
-// (32 rows), n-frag j.
+// Shared main loop.  The block owns a 128-row tile of f16 activation rows and
+// each wave NF 32-column weight fragments.  acc[i][j]: m-frag i (32 rows),
+// n-frag j.
+//
+// Pipeline, per 64-k group g (one scale group):
+//  * activation tile: direct global->LDS loads (global_load_lds_dwordx4) into
+//    a ring of NS = 4 LDS stages, issued 3 groups ahead.  A wave's DMA writes
+//    1 KB of LDS in lane order, so lane l of chunk c fetches the octet that the
+//    XOR swizzle places at slot l%8 of row 8c + l/8.
+//  * packed weights + scales: registers, 4 slots, issued 3 groups ahead.
+//  * one s_barrier per group, preceded by a counted vmcnt wait: each thread
+//    issues exactly LPG loads per group in a fixed order, so allowing the two
+//    newest groups' loads to stay in flight guarantees this group's tile and
+//    weights have landed (near the end, where fewer groups follow, the wait
+//    is vmcnt(0)).  Stage g%4 is rewritten only by the DMA issued after the
+//    barrier of group g+1, when every wave has finished reading it.
 // ---------------------------------------------------------------------------
 template <int NF>
 struct Frags {
     f32x16 acc[4][NF];
 };
 
+#define QMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
 template <int NF>
 __device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *const *arow,
                                               const uint8_t *const *brow,
                                               const float *const *srow, int ng,
-                                              uint16_t *sA /* [2][128*64] */) {
-    const int tid = threadIdx.x, lane = lane_id();
-    const int a_oct = tid & 7;
+                                              uint16_t *__restrict__ s0,
+                                              uint16_t *__restrict__ s1,
+                                              uint16_t *__restrict__ s2,
+                                              uint16_t *__restrict__ s3) {
+    const int lane = lane_id(), w = wave_id();
     const int hh = lane >> 5, nl = lane & 31;
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -155,47 +197,29 @@ __device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *con
 #pragma unroll
             for (int v = 0; v < 16; v++) fr.acc[i][j][v] = 0.f;
 
-    // Registers in flight: the A pieces of the next group, and the packed
-    // weights + scales of the current (slot S) and next (slot 1-S) group.
-    u32x4 ra[4];
-    u32x4 rb[2][NF];
-    float rs[2][NF];
-    auto fetch_a = [&](int g) {
+    u32x4 rb[4][NF];
+    float rs[4][NF];
+    // Issue the tile DMA of group g into stage buffer `buf` (4 loads).
+    auto dma_a = [&](int g, uint16_t *buf) {
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            ra[i] = arow[i] ? *(const u32x4 *)(arow[i] + g * 64) : u32x4{0, 0, 0, 0};
+            __builtin_amdgcn_global_load_lds((const void *)(arow[i] + g * 64),
+                                             QMOE_LDS(buf + (w * 4 + i) * 512), 16, 0, 0);
     };
+    // Issue the weight loads of group g into register slot `slot` (2*NF loads).
     auto fetch_b = [&](int g, int slot) {
 #pragma unroll
         for (int j = 0; j < NF; j++) {
-            if (brow[j]) {
-                rb[slot][j] = *(const u32x4 *)(brow[j] + (int64_t)g * 32);
-                rs[slot][j] = srow[j][g];
-            } else {
-                rb[slot][j] = u32x4{0, 0, 0, 0};
-                rs[slot][j] = 0.f;
-            }
+            rb[slot][j] = *(const u32x4 *)(brow[j] + (int64_t)g * 32);
+            rs[slot][j] = srow[j][g];
         }
     };
-    auto stage_a = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int m = (tid >> 3) + 32 * i;
-            *(u32x4 *)&sA[buf * BM * 64 + sw_off(m, a_oct)] = ra[i];
-        }
-    };
-    // One group: operands A in sA[S], weights in rb[S].
-    auto iter = [&](int g, auto slot_c) {
-        constexpr int S = decltype(slot_c)::value;
-        const bool more = g + 1 < ng;
-        if (more) {
-            fetch_a(g + 1);
-            fetch_b(g + 1, 1 - S);
-        }
+    constexpr int LPG = 4 + 2 * NF;   // loads per thread per group
+    auto compute = [&](int slot, const uint16_t *buf) {
         f16x2 s2[NF];
 #pragma unroll
         for (int j = 0; j < NF; j++) {
-            const _Float16 sh = (_Float16)rs[S][j];
+            const _Float16 sh = (_Float16)rs[slot][j];
             s2[j] = f16x2{sh, sh};
         }
 #pragma unroll
@@ -203,10 +227,10 @@ __device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *con
             f16x8 av[4];
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                av[i] = *(const f16x8 *)&sA[S * BM * 64 + sw_off(32 * i + nl, 4 * hh + kk)];
+                av[i] = *(const f16x8 *)&buf[sw_off(32 * i + nl, 4 * hh + kk)];
             f16x8 bq[NF];
 #pragma unroll
-            for (int j = 0; j < NF; j++) bq[j] = dequant8(rb[S][j][kk], s2[j]);
+            for (int j = 0; j < NF; j++) bq[j] = dequant8(rb[slot][j][kk], s2[j]);
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -214,18 +238,41 @@ __device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *con
                     fr.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[j],
                                                                           fr.acc[i][j], 0, 0, 0);
         }
-        if (more) stage_a(1 - S);
-        __syncthreads();
+    };
+    // Top of group g: wait for its tile and weights, then barrier.
+    auto sync_group = [&](int g) {
+        if (g + 2 < ng) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPG));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_barrier();
+    };
+    auto iter = [&](int g, int slot, uint16_t *cur, uint16_t *ahead) {
+        sync_group(g);
+        if (g + 3 < ng) {
+            dma_a(g + 3, ahead);
+            fetch_b(g + 3, (slot + 3) & 3);
+        }
+        compute(slot, cur);
     };
 
-    fetch_a(0);
+    // prologue: groups 0, 1, 2 in flight (tile and weights of each group)
+    dma_a(0, s0);
     fetch_b(0, 0);
-    stage_a(0);
-    __syncthreads();
-    for (int g = 0; g < ng; g += 2) {
-        iter(g, std::integral_constant<int, 0>{});
-        if (g + 1 < ng) iter(g + 1, std::integral_constant<int, 1>{});
+    if (ng > 1) {
+        dma_a(1, s1);
+        fetch_b(1, 1);
     }
+    if (ng > 2) {
+        dma_a(2, s2);
+        fetch_b(2, 2);
+    }
+    for (int g = 0; g < ng; g += 4) {
+        iter(g, 0, s0, s3);
+        if (g + 1 < ng) iter(g + 1, 1, s1, s0);
+        if (g + 2 < ng) iter(g + 2, 2, s2, s1);
+        if (g + 3 < ng) iter(g + 3, 3, s3, s2);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
 }
 
 // Row (within the tile) held by accumulator v of lane `lane` in m-frag i.
@@ -242,46 +289,43 @@ __device__ __forceinline__ int acc_row(int i, int v, int lane) {
 __global__ void __launch_bounds__(MF_THREADS, 2) mfma_gateup_kernel(
     QMat G, QMat Up, const uint16_t *__restrict__ x16, const float *__restrict__ xinv,
     uint16_t *__restrict__ h16, MfmaRoute r) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * BM * 64];
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[BM * 64], s1[BM * 64], s2[BM * 64],
+        s3[BM * 64];
     __shared__ float sInv[BM];
 
-    TileInfo ti;
-    if (!tile_info(r, blockIdx.y, ti)) return;
     const int H = G.cols, F = G.rows, ng = H / 64;
+    int tile, cb;
+    if (!work_item(r, (F + 127) / 128, tile, cb)) return;
+    TileInfo ti;
+    if (!tile_info(r, tile, ti)) return;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-    const int n = blockIdx.x * 128 + 32 * w + (lane & 31);
-    const bool wave_on = blockIdx.x * 128 + 32 * w < F;
+    const int n = cb * 128 + 32 * w + (lane & 31);
+    const bool wave_on = cb * 128 + 32 * w < F;
+    auto token = [&](int m) -> int64_t {
+        return r.wl.pairs ? r.wl.pairs[ti.pos0 + m] / r.k : ti.pos0 + m;
+    };
 
+    // Tile DMA sources: chunk 4w+i holds rows 8(4w+i) + lane/8, swizzle slot lane%8.
     const uint16_t *arow[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int m = (tid >> 3) + 32 * i;
-        arow[i] = nullptr;
-        if (m < ti.rows) {
-            const int64_t t = r.wl.pairs ? r.wl.pairs[ti.pos0 + m] / r.k : ti.pos0 + m;
-            arow[i] = x16 + t * H + (tid & 7) * 8;
-        }
+        int m = 8 * (4 * w + i) + (lane >> 3);
+        const int oct = (lane & 7) ^ ((lane >> 3) & 7);
+        if (m >= ti.rows) m = 0;          // padding rows: any valid row, never stored
+        arow[i] = x16 + token(m) * H + oct * 8;
     }
-    if (tid < BM) {
-        float v = 0.f;
-        if (tid < ti.rows) {
-            const int64_t t = r.wl.pairs ? r.wl.pairs[ti.pos0 + tid] / r.k : ti.pos0 + tid;
-            v = xinv[t];
-        }
-        sInv[tid] = v;
-    }
+    if (tid < BM) sInv[tid] = tid < ti.rows ? xinv[token(tid)] : 0.f;
     const uint8_t *brow[2];
     const float *srow[2];
     const int hh = lane >> 5;
-    brow[0] = wave_on ? G.q + (int64_t)ti.e * G.q_stride + (int64_t)n * (H / 2) + 16 * hh
-                      : nullptr;
-    brow[1] = wave_on ? Up.q + (int64_t)ti.e * Up.q_stride + (int64_t)n * (H / 2) + 16 * hh
-                      : nullptr;
-    srow[0] = G.s + (int64_t)ti.e * G.s_stride + (int64_t)(wave_on ? n : 0) * ng;
-    srow[1] = Up.s + (int64_t)ti.e * Up.s_stride + (int64_t)(wave_on ? n : 0) * ng;
+    const int nn = wave_on ? n : 0;       // idle waves read row 0 (valid) and store nothing
+    brow[0] = G.q + (int64_t)ti.e * G.q_stride + (int64_t)nn * (H / 2) + 16 * hh;
+    brow[1] = Up.q + (int64_t)ti.e * Up.q_stride + (int64_t)nn * (H / 2) + 16 * hh;
+    srow[0] = G.s + (int64_t)ti.e * G.s_stride + (int64_t)nn * ng;
+    srow[1] = Up.s + (int64_t)ti.e * Up.s_stride + (int64_t)nn * ng;
 
     Frags<2> fr;
-    mfma_mainloop<2>(fr, arow, brow, srow, ng, sA);
+    mfma_mainloop<2>(fr, arow, brow, srow, ng, s0, s1, s2, s3);
 
     if (!wave_on) return;
     const int npos = (n & ~7) + octet_pos(n & 7);
@@ -291,8 +335,8 @@ __global__ void __launch_bounds__(MF_THREADS, 2) mfma_gateup_kernel(
         for (int v = 0; v < 16; v++) {
             const int m = acc_row(i, v, lane);
             if (m < ti.rows) {
-                const float s = sInv[m];
-                const float h = silu(fr.acc[i][0][v] * s) * (fr.acc[i][1][v] * s);
+                const float sc = sInv[m];
+                const float h = silu(fr.acc[i][0][v] * sc) * (fr.acc[i][1][v] * sc);
                 h16[(int64_t)(ti.pos0 + m) * F + npos] =
                     __builtin_bit_cast(uint16_t, (_Float16)h);
             }
@@ -309,34 +353,38 @@ __global__ void __launch_bounds__(MF_THREADS, 2) mfma_down_kernel(QMat D,
                                                                   const uint16_t *__restrict__ h16,
                                                                   float *__restrict__ y,
                                                                   MfmaRoute r) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * BM * 64];
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[BM * 64], s1[BM * 64], s2[BM * 64],
+        s3[BM * 64];
 
-    TileInfo ti;
-    if (!tile_info(r, blockIdx.y, ti)) return;
     const int H = D.rows, F = D.cols, ng = F / 64;
-    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    int tile, cb;
+    if (!work_item(r, (H + 255) / 256, tile, cb)) return;
+    TileInfo ti;
+    if (!tile_info(r, tile, ti)) return;
+    const int lane = lane_id(), w = wave_id();
     const int hh = lane >> 5;
 
     const uint16_t *arow[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int m = (tid >> 3) + 32 * i;
-        arow[i] = m < ti.rows ? h16 + (int64_t)(ti.pos0 + m) * F + (tid & 7) * 8 : nullptr;
+        int m = 8 * (4 * w + i) + (lane >> 3);
+        const int oct = (lane & 7) ^ ((lane >> 3) & 7);
+        if (m >= ti.rows) m = 0;
+        arow[i] = h16 + (int64_t)(ti.pos0 + m) * F + oct * 8;
     }
     const uint8_t *brow[2];
     const float *srow[2];
     int ncol[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
-        ncol[j] = blockIdx.x * 256 + 64 * w + 32 * j + (lane & 31);
-        const bool on = ncol[j] < H;
-        brow[j] = on ? D.q + (int64_t)ti.e * D.q_stride + (int64_t)ncol[j] * (F / 2) + 16 * hh
-                     : nullptr;
-        srow[j] = D.s + (int64_t)ti.e * D.s_stride + (int64_t)(on ? ncol[j] : 0) * ng;
+        ncol[j] = cb * 256 + 64 * w + 32 * j + (lane & 31);
+        const int nn = ncol[j] < H ? ncol[j] : 0;
+        brow[j] = D.q + (int64_t)ti.e * D.q_stride + (int64_t)nn * (F / 2) + 16 * hh;
+        srow[j] = D.s + (int64_t)ti.e * D.s_stride + (int64_t)nn * ng;
     }
 
     Frags<2> fr;
-    mfma_mainloop<2>(fr, arow, brow, srow, ng, sA);
+    mfma_mainloop<2>(fr, arow, brow, srow, ng, s0, s1, s2, s3);
 
     const bool routed = r.wl.pairs != nullptr;
 #pragma unroll
@@ -380,7 +428,7 @@ hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *
                               const float *xinv, uint16_t *h16, const MfmaRoute &r,
                               hipStream_t st) {
     const int ntiles = r.wl.pairs ? r.max_tiles : (r.ntok + BM - 1) / BM;
-    const dim3 grid((gate.rows + 127) / 128, ntiles);
+    const dim3 grid(xcd_grid((int64_t)ntiles * ((gate.rows + 127) / 128)));
     hipLaunchKernelGGL(mfma_gateup_kernel, grid, dim3(MF_THREADS), 0, st, gate, up, x16, xinv,
                        h16, r);
     return hipGetLastError();
@@ -389,7 +437,7 @@ hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *
 hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y, const MfmaRoute &r,
                             hipStream_t st) {
     const int ntiles = r.wl.pairs ? r.max_tiles : (r.ntok + BM - 1) / BM;
-    const dim3 grid((down.rows + 255) / 256, ntiles);
+    const dim3 grid(xcd_grid((int64_t)ntiles * ((down.rows + 255) / 256)));
     hipLaunchKernelGGL(mfma_down_kernel, grid, dim3(MF_THREADS), 0, st, down, h16, y, r);
     return hipGetLastError();
 }
