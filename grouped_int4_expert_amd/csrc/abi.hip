@@ -30,6 +30,13 @@ inline bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
 
 inline int status_of(hipError_t e) { return e == hipSuccess ? QMOE_OK : QMOE_ERR_HIP; }
 
+// The prefill kernels address activations, h and each expert's weights
+// through buffer descriptors with 32-bit byte sizes and offsets.
+inline bool mfma_fits(int64_t H, int64_t F, int64_t x_rows, int64_t h_rows) {
+    const int64_t lim = (int64_t)1 << 32;
+    return x_rows * H * 2 < lim && h_rows * F * 2 < lim && H * F / 2 < lim && H * F / 16 < lim;
+}
+
 int64_t packed_bytes(int64_t rows, int64_t cols) { return rows * ((cols + 1) / 2); }
 int64_t scale_count(int64_t rows, int64_t cols, int64_t g) { return rows * ((cols + g - 1) / g); }
 
@@ -309,6 +316,9 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
         r.wl.pairs = nullptr;
         r.ntok = batch;
         r.k = 1;
+        r.x_rows = batch;
+        r.h_rows = batch;
+        if (!mfma_fits(H, F, batch, batch)) return QMOE_ERR_SHAPE;
         e = launch_xprep(static_cast<const uint16_t *>(x), batch, H, x16, xinv, st);
         if (e == hipSuccess)
             e = launch_mfma_gateup(to_qmat(gate), to_qmat(up), x16, xinv, h16, r, st);
@@ -399,6 +409,7 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         const int64_t n0 = (int64_t)tokens * k;
         const int64_t tiles = (n0 + MFMA_BM - 1) / MFMA_BM + (n0 < E ? n0 : E);
         if (tiles > 65535) return QMOE_ERR_SHAPE;   // grid.y bound of the tiled kernels
+        if (x_dtype == QMOE_BF16 && !mfma_fits(H, F, tokens, n0)) return QMOE_ERR_SHAPE;
     }
     if (phase_events) {
         if (n_events < (x_dtype == QMOE_F32 ? 4 : 5)) return QMOE_ERR_SHAPE;
@@ -458,6 +469,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         r.topk_w = topk_w;
         r.k = k;
         r.max_tiles = L.max_tiles;
+        r.x_rows = tokens;
+        r.h_rows = n;
         if (e == hipSuccess) e = launch_mfma_gateup(G, U, L.x16, L.xinv, L.h16, r, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_mfma_down(D, L.h16, L.y, r, st);

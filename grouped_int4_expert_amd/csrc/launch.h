@@ -91,13 +91,15 @@ hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
                               hipStream_t st);
 
 // Prefill (bf16 activations, MFMA).
-constexpr int MFMA_BM = 128;
+constexpr int MFMA_BM = 256;
 struct MfmaRoute {
     Worklist wl;
     const float *topk_w;
     int k;
     int max_tiles;     // grid bound on tiles
     int ntok;          // direct mode
+    int64_t x_rows;    // rows of x16 (tokens); x_rows * hidden * 2 < 2^32
+    int64_t h_rows;    // rows of h16 (pair positions); h_rows * inter * 2 < 2^32
 };
 // x bf16 [tokens][hidden] -> x16 f16 scaled by 2^k_t (octet-permuted), xinv = 2^-k_t.
 hipError_t launch_xprep(const uint16_t *x, int tokens, int hidden, uint16_t *x16, float *xinv,

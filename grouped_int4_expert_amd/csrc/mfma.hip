@@ -8,7 +8,7 @@
 // not a design).  The design here is MI355X's own:
 //
 //  * Tiles come from the device worklist: (expert, first sorted row), at
-//    most 128 rows each; activation rows are gathered through the sorted
+//    most 256 rows each; activation rows are gathered through the sorted
 //    pair list.
 //  * A one-pass prep turns each bf16 activation row into f16 scaled by a
 //    power of two 2^k_t (so the row maximum sits in [2^14, 2^15); bf16 -> f16
@@ -22,8 +22,10 @@
 //    the exact code, packed multiply by the f16 group scale), so the f32
 //    group scale costs no per-group accumulator work; rounding q*s to f16
 //    adds ~2^-12 relative error per weight (bf16 would be 2^-9).
-//  * v_mfma_f32_32x32x16_f16; block = 4 waves x (128 rows x 32 features of
-//    gate and of up) or 4 waves x (128 rows x 64 features) for down; the
+//  * v_mfma_f32_32x32x16_f16; block = 4 waves x (256 rows x 32 features of
+//    gate and of up) or 4 waves x (256 rows x 64 features) for down, so each
+//    unpacked weight fragment feeds 8 row fragments (accumulators live in
+//    AGPRs); row fragments past the tile's rows are skipped; the
 //    activation tile (128 x 64 f16 per group) is double-buffered in LDS with
 //    octets XOR-swizzled by row; global loads of group g+1 are issued
 //    before the MFMAs of group g, and two blocks per CU overlap waits.
@@ -35,9 +37,20 @@
 namespace qmoe {
 
 constexpr int MF_THREADS = 256;
-constexpr int BM = MFMA_BM;   // 128 token rows per tile
+constexpr int BM = MFMA_BM;   // token rows per worklist tile
+// A block takes BMK rows: a whole tile or a part of it (BM / BMK parts).
+template <int BMK>
+constexpr int mf_of() { return BMK / 32; }   // 32-row MFMA fragments per block
+template <int BMK>
+constexpr int occ_of() { return BMK > 128 ? 1 : 2; }   // blocks per CU
+// gate+up takes whole 256-row tiles (each unpacked weight fragment feeds 8
+// row fragments; one block per CU); down, with a third of the k-depth and
+// four times the output bytes per row, takes half tiles at two blocks per
+// CU so one block's prologue and stores overlap the other's MFMAs.
+constexpr int GATEUP_BM = 256;
+constexpr int DOWN_BM = 128;
 
-// LDS offset (in 16-bit elements) of octet `o` of row `m` in a 128 x 64 tile.
+// LDS offset (in 16-bit elements) of octet `o` of row `m` in a BMK x 64 tile.
 __device__ __forceinline__ int sw_off(int m, int o) { return m * 64 + ((o ^ (m & 7)) << 3); }
 
 // s_waitcnt immediate (gfx9 layout) that waits until at most n vector memory
@@ -49,13 +62,20 @@ __host__ __device__ constexpr int waitcnt_vm(int n) {
 // Position of element e (0..7) of an octet after the unpack permutation.
 __device__ __forceinline__ int octet_pos(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
 
-// 8 packed codes (one dword) -> 8 f16 values q*s in unpack order.
+// 8 packed codes (one dword) -> 8 f16 values q*s in unpack order.  Pair i
+// (nibbles i and 4+i) lands in the mantissas of two f16 1024.0 with one
+// and-or (mask and exponent bits held in registers, so the compiler can use
+// the 3-operand form), then a packed add of -1032 gives the exact code and a
+// packed multiply applies the group scale.
 __device__ __forceinline__ f16x8 dequant8(uint32_t d, f16x2 s2) {
+    uint32_t mask = 0x000F000Fu, expo = 0x64006400u;
+    asm("" : "+v"(mask));
+    asm("" : "+v"(expo));
     const f16x2 off = {(_Float16)-1032.0f, (_Float16)-1032.0f};
     f16x8 r;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const uint32_t t = ((d >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+        const uint32_t t = ((d >> (4 * i)) & mask) | expo;
         const f16x2 v = (__builtin_bit_cast(f16x2, t) + off) * s2;
         r[2 * i] = v[0];
         r[2 * i + 1] = v[1];
@@ -67,22 +87,28 @@ struct TileInfo {
     int e, row0, rows, pos0;
 };
 
-__device__ __forceinline__ bool tile_info(const MfmaRoute &r, int tile, TileInfo &ti) {
+// Rows of block item `item`: part item % (BM / BMK) of worklist tile
+// item / (BM / BMK); direct mode has plain BMK-row items.
+template <int BMK>
+__device__ __forceinline__ bool tile_info(const MfmaRoute &r, int item, TileInfo &ti) {
     if (r.wl.pairs == nullptr) {
-        const int row0 = tile * BM;
+        const int row0 = item * BMK;
         if (row0 >= r.ntok) return false;
         ti.e = 0;
         ti.row0 = row0;
         ti.pos0 = row0;
-        ti.rows = min(BM, r.ntok - row0);
+        ti.rows = min(BMK, r.ntok - row0);
         return true;
     }
+    constexpr int SPLIT = BM / BMK;
+    const int tile = item / SPLIT, part = item - tile * SPLIT;
     if (tile >= r.wl.n_tiles[0]) return false;
     ti.e = r.wl.tiles[2 * tile];
-    ti.row0 = r.wl.tiles[2 * tile + 1];
+    ti.row0 = r.wl.tiles[2 * tile + 1] + part * BMK;
     const int c = r.wl.counts[ti.e];
+    if (ti.row0 >= c) return false;
     ti.pos0 = r.wl.offsets[ti.e] + ti.row0;
-    ti.rows = min(BM, c - ti.row0);
+    ti.rows = min(BMK, c - ti.row0);
     return true;
 }
 
@@ -92,8 +118,9 @@ __device__ __forceinline__ bool tile_info(const MfmaRoute &r, int tile, TileInfo
 // device worklist), column blocks of a tile adjacent: a tile's activation
 // rows and an expert's weight slices are then fetched into one L2 instead of
 // up to eight.  gridDim.x is a multiple of 8 and >= the largest item count.
+template <int BMK>
 __device__ __forceinline__ bool work_item(const MfmaRoute &r, int ncb, int &tile, int &cb) {
-    const int ntiles = r.wl.pairs ? r.wl.n_tiles[0] : (r.ntok + BM - 1) / BM;
+    const int ntiles = r.wl.pairs ? r.wl.n_tiles[0] * (BM / BMK) : (r.ntok + BMK - 1) / BMK;
     const int W = ntiles * ncb;
     const int per_xcd = (W + 7) / 8;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -156,42 +183,88 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Shared main loop.  The block owns a 128-row tile of f16 activation rows and
-// each wave NF 32-column weight fragments.  acc[i][j]: m-frag i (32 rows),
-// n-frag j.
+// Shared main loop.  The block owns a BM-row tile of f16 activation rows and
+// each wave NF = 2 column fragments of 32 weight rows.  acc[i][j]: row
+// fragment i (32 rows), column fragment j.  MFC (8 or 4) row fragments are
+// computed; a tile of at most 128 rows takes the MFC = 4 instance.
 //
-// Pipeline, per 64-k group g (one scale group):
-//  * activation tile: direct global->LDS loads (global_load_lds_dwordx4) into
-//    a ring of NS = 4 LDS stages, issued 3 groups ahead.  A wave's DMA writes
-//    1 KB of LDS in lane order, so lane l of chunk c fetches the octet that the
-//    XOR swizzle places at slot l%8 of row 8c + l/8.
-//  * packed weights + scales: registers, 4 slots, issued 3 groups ahead.
-//  * one s_barrier per group, preceded by a counted vmcnt wait: each thread
-//    issues exactly LPG loads per group in a fixed order, so allowing the two
-//    newest groups' loads to stay in flight guarantees this group's tile and
-//    weights have landed (near the end, where fewer groups follow, the wait
-//    is vmcnt(0)).  Stage g%4 is rewritten only by the DMA issued after the
-//    barrier of group g+1, when every wave has finished reading it.
+// All global reads are buffer loads: the 128-bit descriptor (base, byte
+// size) sits in scalar registers, each lane keeps a 32-bit byte offset, and
+// the per-group advance is the scalar offset operand, so the loop spends no
+// vector instructions on addresses; reads past the descriptor's size return 0.
+//
+// Pipeline.  A 64-k group g (one scale group) is 4 k-steps of 16:
+//  * activation tile: buffer loads straight into LDS (16 B per lane) into a
+//    ring of 4 LDS stages.  One such load of a wave writes 1 KB of LDS in
+//    lane order; load i of wave w fills rows 32i + 8w + lane/8 (row fragment
+//    i), and lane l fetches the octet that the XOR swizzle places at slot l%8
+//    of its row.
+//  * packed weights + scales: registers, 4 slots.
+//  * operands of k-step s+1 (LDS reads of the activation fragments, unpack
+//    of the weight fragments) are produced while the MFMAs of step s run;
+//    with one wave per SIMD nothing else hides their latency, so the
+//    instruction scheduler is told to interleave them (1 MFMA, 1 LDS read,
+//    a few VALU ops, repeated).
+//  * group g+1 is synchronised just before the last k-step of group g:
+//    counted vmcnt wait (each thread issues exactly MFC + 2*NF loads per
+//    group in a fixed order, so letting the two newest groups' loads stay in
+//    flight guarantees group g+1 has landed), then one s_barrier.  Every
+//    wave has by then finished its LDS reads of stage g, so the loads of
+//    group g+4 into that stage are issued right after the barrier, and the
+//    last k-step's MFMAs overlap group g+1's first operand reads.
 // ---------------------------------------------------------------------------
-template <int NF>
+constexpr int NF = 2;
+
+template <int MF>
 struct Frags {
-    f32x16 acc[4][NF];
+    f32x16 acc[MF][NF];
+};
+
+// Buffer descriptor over [base, base + bytes); bytes < 2^32 is checked by
+// the host.  Word 3 selects 32-bit data format, as raw loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(uint32_t)bytes, 0x00020000);
+}
+
+// Sources of one block: activation tile (one descriptor, MF lane offsets at
+// group 0) and the wave's two weight column fragments.
+template <int MF>
+struct LoopSrc {
+    __amdgpu_buffer_rsrc_t a;
+    uint32_t aoff[MF];
+    __amdgpu_buffer_rsrc_t q[NF], s[NF];
+    uint32_t qoff[NF], soff[NF];
 };
 
 #define QMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-template <int NF>
-__device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *const *arow,
-                                              const uint8_t *const *brow,
-                                              const float *const *srow, int ng,
+// Scheduling hint for one k-step: n_mfma MFMAs, each followed by one LDS
+// read (while any remain) and `valu` VALU instructions.
+template <int N_MFMA, int N_DS, int VALU>
+__device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+    for (int t = 0; t < N_MFMA; t++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t < N_DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+    }
+}
+
+template <int MF, int MFC>
+__device__ __forceinline__ void mfma_mainloop(Frags<MF> &fr, const LoopSrc<MF> &src, int ng,
                                               uint16_t *__restrict__ s0,
                                               uint16_t *__restrict__ s1,
                                               uint16_t *__restrict__ s2,
                                               uint16_t *__restrict__ s3) {
-    const int lane = lane_id(), w = wave_id();
+    static_assert(MFC <= MF, "row fragments");
+    constexpr int LPG = MFC + 2 * NF;   // loads per thread per group, in issue order
+    constexpr int VALU_PER_MFMA = (40 + MFC * NF - 1) / (MFC * NF);
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int hh = lane >> 5, nl = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < MFC; i++)
 #pragma unroll
         for (int j = 0; j < NF; j++)
 #pragma unroll
@@ -199,78 +272,88 @@ __device__ __forceinline__ void mfma_mainloop(Frags<NF> &fr, const uint16_t *con
 
     u32x4 rb[4][NF];
     float rs[4][NF];
-    // Issue the tile DMA of group g into stage buffer `buf` (4 loads).
-    auto dma_a = [&](int g, uint16_t *buf) {
+    f16x8 av[2][MFC], bq[2][NF];
+    f16x2 sc[NF];
+    // Loads of group g (clamped to the last real group; the padding groups
+    // past ng get a zero scale) into register slot `slot` and LDS stage buf.
+    auto issue_loads = [&](int g, int slot, uint16_t *buf) {
+        const int gc = g < ng ? g : ng - 1;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            __builtin_amdgcn_global_load_lds((const void *)(arow[i] + g * 64),
-                                             QMOE_LDS(buf + (w * 4 + i) * 512), 16, 0, 0);
-    };
-    // Issue the weight loads of group g into register slot `slot` (2*NF loads).
-    auto fetch_b = [&](int g, int slot) {
-#pragma unroll
-        for (int j = 0; j < NF; j++) {
-            rb[slot][j] = *(const u32x4 *)(brow[j] + (int64_t)g * 32);
-            rs[slot][j] = srow[j][g];
-        }
-    };
-    constexpr int LPG = 4 + 2 * NF;   // loads per thread per group
-    auto compute = [&](int slot, const uint16_t *buf) {
-        f16x2 s2[NF];
+        for (int i = 0; i < MFC; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, QMOE_LDS(buf + (i * 4 + w) * 512), 16,
+                                                     src.aoff[i], gc * 128, 0, 0);
 #pragma unroll
         for (int j = 0; j < NF; j++) {
-            const _Float16 sh = (_Float16)rs[slot][j];
-            s2[j] = f16x2{sh, sh};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; kk++) {
-            f16x8 av[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                av[i] = *(const f16x8 *)&buf[sw_off(32 * i + nl, 4 * hh + kk)];
-            f16x8 bq[NF];
-#pragma unroll
-            for (int j = 0; j < NF; j++) bq[j] = dequant8(rb[slot][j][kk], s2[j]);
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < NF; j++)
-                    fr.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bq[j],
-                                                                          fr.acc[i][j], 0, 0, 0);
+            rb[slot][j] = __builtin_amdgcn_raw_buffer_load_b128(src.q[j], src.qoff[j], gc * 32, 0);
+            rs[slot][j] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(src.s[j], src.soff[j], gc * 4, 0));
         }
     };
-    // Top of group g: wait for its tile and weights, then barrier.
-    auto sync_group = [&](int g) {
-        if (g + 2 < ng) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPG));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // Operands of k-step kk of group g (ring slot/stage `slot`, buf) into
+    // operand buffer p.
+    auto operands = [&](int p, int g, int slot, const uint16_t *buf, int kk) {
+        if (kk == 0) {
+#pragma unroll
+            for (int j = 0; j < NF; j++) {
+                const _Float16 sh = g < ng ? (_Float16)rs[slot][j] : (_Float16)0.0f;
+                sc[j] = f16x2{sh, sh};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MFC; i++)
+            av[p][i] = *(const f16x8 *)&buf[sw_off(32 * i + nl, 4 * hh + kk)];
+#pragma unroll
+        for (int j = 0; j < NF; j++) bq[p][j] = dequant8(rb[slot][j][kk], sc[j]);
+    };
+    auto mfmas = [&](int p) {
+#pragma unroll
+        for (int i = 0; i < MFC; i++)
+#pragma unroll
+            for (int j = 0; j < NF; j++)
+                fr.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[p][i], bq[p][j],
+                                                                     fr.acc[i][j], 0, 0, 0);
+    };
+    // Group g (ring slot/stage `slot`, stages cur and next): k-steps 0..2
+    // prefetch the next step's operands; before step 3, group g+1 is
+    // synchronised (this wave's LDS reads of cur are done, every thread's
+    // loads of group g+1 have landed, barrier), group g+4's loads go into
+    // cur, and step 3 prefetches group g+1's first operands.  Nothing here
+    // is conditional, so no register holding an in-flight load is ever
+    // copied (a copy would wait for the load).
+    auto group = [&](int g, int slot, uint16_t *cur, uint16_t *next) {
+#pragma unroll
+        for (int kk = 0; kk < 3; kk++) {
+            operands((kk + 1) & 1, g, slot, cur, kk + 1);
+            mfmas(kk & 1);
+            interleave_hint<MFC * NF, MFC, VALU_PER_MFMA>();
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPG));
         __builtin_amdgcn_s_barrier();
-    };
-    auto iter = [&](int g, int slot, uint16_t *cur, uint16_t *ahead) {
-        sync_group(g);
-        if (g + 3 < ng) {
-            dma_a(g + 3, ahead);
-            fetch_b(g + 3, (slot + 3) & 3);
-        }
-        compute(slot, cur);
+        issue_loads(g + 4, slot, cur);
+        operands(0, g + 1, (slot + 1) & 3, next, 0);
+        mfmas(1);
+        interleave_hint<MFC * NF, MFC, VALU_PER_MFMA>();
     };
 
-    // prologue: groups 0, 1, 2 in flight (tile and weights of each group)
-    dma_a(0, s0);
-    fetch_b(0, 0);
-    if (ng > 1) {
-        dma_a(1, s1);
-        fetch_b(1, 1);
-    }
-    if (ng > 2) {
-        dma_a(2, s2);
-        fetch_b(2, 2);
-    }
+    // Prologue: groups 0..2 in flight, group 0 synchronised, group 3 issued,
+    // operands of group 0 step 0 read.  The loop runs ng rounded up to a
+    // multiple of 4 groups; loads past the end re-read the last group and
+    // the padding groups multiply by a zero scale.
+    issue_loads(0, 0, s0);
+    issue_loads(1, 1, s1);
+    issue_loads(2, 2, s2);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPG));
+    __builtin_amdgcn_s_barrier();
+    issue_loads(3, 3, s3);
+    operands(0, 0, 0, s0, 0);
     for (int g = 0; g < ng; g += 4) {
-        iter(g, 0, s0, s3);
-        if (g + 1 < ng) iter(g + 1, 1, s1, s0);
-        if (g + 2 < ng) iter(g + 2, 2, s2, s1);
-        if (g + 3 < ng) iter(g + 3, 3, s3, s2);
+        group(g, 0, s0, s1);
+        group(g + 1, 1, s1, s2);
+        group(g + 2, 2, s2, s3);
+        group(g + 3, 3, s3, s0);
     }
+    // no load may still be writing LDS when the block ends
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
 }
@@ -280,24 +363,55 @@ __device__ __forceinline__ int acc_row(int i, int v, int lane) {
     return 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
+// Runs the main loop over the row fragments a tile of `rows` rows needs
+// (rounded up to MF, MF/2 or MF/4 fragments).
+template <int MF>
+__device__ __forceinline__ void run_mainloop(Frags<MF> &fr, const LoopSrc<MF> &src, int ng, int rows,
+                                             uint16_t *__restrict__ s0,
+                                             uint16_t *__restrict__ s1,
+                                             uint16_t *__restrict__ s2,
+                                             uint16_t *__restrict__ s3) {
+    if (rows > 16 * MF) mfma_mainloop<MF, MF>(fr, src, ng, s0, s1, s2, s3);
+    else if (rows > 8 * MF) mfma_mainloop<MF, MF / 2>(fr, src, ng, s0, s1, s2, s3);
+    else mfma_mainloop<MF, MF / 4>(fr, src, ng, s0, s1, s2, s3);
+}
+
+// Activation tile sources: load i of wave w fills rows 32i + 8w + lane/8,
+// whose swizzle slot lane%8 holds octet (lane%8) ^ (row%8).  Rows past the
+// tile read a valid row (row 0) and are never stored.
+template <int MF, typename RowOf>
+__device__ __forceinline__ void tile_offsets(LoopSrc<MF> &src, int rows, int row_elems,
+                                             RowOf row_of) {
+    const int lane = lane_id(), w = wave_id();
+    const int oct = (lane & 7) ^ ((lane >> 3) & 7);
+#pragma unroll
+    for (int i = 0; i < MF; i++) {
+        int m = 32 * i + 8 * w + (lane >> 3);
+        if (m >= rows) m = 0;
+        src.aoff[i] = (uint32_t)(row_of(m) * row_elems * 2 + oct * 16);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// gate+up: block = (128 features of F for gate and up, one tile of <=128
+// gate+up: block = (128 features of F for gate and up, one tile of <=256
 // rows).  Wave w: features n0 + 32w .. +32 of gate (frag 0) and up (frag 1).
 // Output h = silu(g) * u as f16 at sorted position pos0 + m, octet-permuted
 // in the feature index (the down projection's k).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(MF_THREADS, 2) mfma_gateup_kernel(
+template <int BMK>
+__global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_gateup_kernel(
     QMat G, QMat Up, const uint16_t *__restrict__ x16, const float *__restrict__ xinv,
     uint16_t *__restrict__ h16, MfmaRoute r) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[BM * 64], s1[BM * 64], s2[BM * 64],
-        s3[BM * 64];
-    __shared__ float sInv[BM];
+    constexpr int MF = mf_of<BMK>();
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
+        s2[BMK * 64], s3[BMK * 64];
+    __shared__ float sInv[BMK];
 
     const int H = G.cols, F = G.rows, ng = H / 64;
     int tile, cb;
-    if (!work_item(r, (F + 127) / 128, tile, cb)) return;
+    if (!work_item<BMK>(r, (F + 127) / 128, tile, cb)) return;
     TileInfo ti;
-    if (!tile_info(r, tile, ti)) return;
+    if (!tile_info<BMK>(r, tile, ti)) return;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     const int n = cb * 128 + 32 * w + (lane & 31);
     const bool wave_on = cb * 128 + 32 * w < F;
@@ -305,32 +419,29 @@ __global__ void __launch_bounds__(MF_THREADS, 2) mfma_gateup_kernel(
         return r.wl.pairs ? r.wl.pairs[ti.pos0 + m] / r.k : ti.pos0 + m;
     };
 
-    // Tile DMA sources: chunk 4w+i holds rows 8(4w+i) + lane/8, swizzle slot lane%8.
-    const uint16_t *arow[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int m = 8 * (4 * w + i) + (lane >> 3);
-        const int oct = (lane & 7) ^ ((lane >> 3) & 7);
-        if (m >= ti.rows) m = 0;          // padding rows: any valid row, never stored
-        arow[i] = x16 + token(m) * H + oct * 8;
-    }
-    if (tid < BM) sInv[tid] = tid < ti.rows ? xinv[token(tid)] : 0.f;
-    const uint8_t *brow[2];
-    const float *srow[2];
+    LoopSrc<MF> src;
+    src.a = make_rsrc(x16, (int64_t)r.x_rows * H * 2);
+    tile_offsets(src, ti.rows, H, token);
+    for (int m = tid; m < BMK; m += MF_THREADS) sInv[m] = m < ti.rows ? xinv[token(m)] : 0.f;
     const int hh = lane >> 5;
     const int nn = wave_on ? n : 0;       // idle waves read row 0 (valid) and store nothing
-    brow[0] = G.q + (int64_t)ti.e * G.q_stride + (int64_t)nn * (H / 2) + 16 * hh;
-    brow[1] = Up.q + (int64_t)ti.e * Up.q_stride + (int64_t)nn * (H / 2) + 16 * hh;
-    srow[0] = G.s + (int64_t)ti.e * G.s_stride + (int64_t)nn * ng;
-    srow[1] = Up.s + (int64_t)ti.e * Up.s_stride + (int64_t)nn * ng;
+    const QMat *mats[NF] = {&G, &Up};
+#pragma unroll
+    for (int j = 0; j < NF; j++) {
+        const QMat &M = *mats[j];
+        src.q[j] = make_rsrc(M.q + (int64_t)ti.e * M.q_stride, (int64_t)F * (H / 2));
+        src.s[j] = make_rsrc(M.s + (int64_t)ti.e * M.s_stride, (int64_t)F * ng * 4);
+        src.qoff[j] = (uint32_t)(nn * (H / 2) + 16 * hh);
+        src.soff[j] = (uint32_t)(nn * ng * 4);
+    }
 
-    Frags<2> fr;
-    mfma_mainloop<2>(fr, arow, brow, srow, ng, s0, s1, s2, s3);
+    Frags<MF> fr;
+    run_mainloop<MF>(fr, src, ng, ti.rows, s0, s1, s2, s3);
 
     if (!wave_on) return;
     const int npos = (n & ~7) + octet_pos(n & 7);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < MF; i++) {
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int m = acc_row(i, v, lane);
@@ -345,58 +456,58 @@ __global__ void __launch_bounds__(MF_THREADS, 2) mfma_gateup_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// down: block = (256 features of H, one tile of <=128 rows); wave w:
+// down: block = (256 features of H, one tile of <=256 rows); wave w:
 // features n0 + 64w + 32j + (lane%32), j = 0, 1.
 // Routed: Y[pos] = w * (D h); direct: out[pos] = D h.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(MF_THREADS, 2) mfma_down_kernel(QMat D,
-                                                                  const uint16_t *__restrict__ h16,
-                                                                  float *__restrict__ y,
-                                                                  MfmaRoute r) {
-    __shared__ __attribute__((aligned(1024))) uint16_t s0[BM * 64], s1[BM * 64], s2[BM * 64],
-        s3[BM * 64];
+template <int BMK>
+__global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
+    QMat D, const uint16_t *__restrict__ h16, float *__restrict__ y, MfmaRoute r) {
+    constexpr int MF = mf_of<BMK>();
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
+        s2[BMK * 64], s3[BMK * 64];
+    __shared__ float sW[BMK];
 
     const int H = D.rows, F = D.cols, ng = F / 64;
     int tile, cb;
-    if (!work_item(r, (H + 255) / 256, tile, cb)) return;
+    if (!work_item<BMK>(r, (H + 255) / 256, tile, cb)) return;
     TileInfo ti;
-    if (!tile_info(r, tile, ti)) return;
-    const int lane = lane_id(), w = wave_id();
+    if (!tile_info<BMK>(r, tile, ti)) return;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
     const int hh = lane >> 5;
+    const bool routed = r.wl.pairs != nullptr;
+    // routing weight of each row, fetched before the main loop (the barriers
+    // inside it publish sW)
+    for (int m = tid; m < BMK; m += MF_THREADS)
+        sW[m] = m >= ti.rows ? 0.f : routed ? r.topk_w[r.wl.pairs[ti.pos0 + m]] : 1.0f;
 
-    const uint16_t *arow[4];
+    LoopSrc<MF> src;
+    src.a = make_rsrc(h16, (int64_t)r.h_rows * F * 2);
+    tile_offsets(src, ti.rows, F, [&](int m) -> int64_t { return ti.pos0 + m; });
+    int ncol[NF];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int m = 8 * (4 * w + i) + (lane >> 3);
-        const int oct = (lane & 7) ^ ((lane >> 3) & 7);
-        if (m >= ti.rows) m = 0;
-        arow[i] = h16 + (int64_t)(ti.pos0 + m) * F + oct * 8;
-    }
-    const uint8_t *brow[2];
-    const float *srow[2];
-    int ncol[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
+    for (int j = 0; j < NF; j++) {
         ncol[j] = cb * 256 + 64 * w + 32 * j + (lane & 31);
         const int nn = ncol[j] < H ? ncol[j] : 0;
-        brow[j] = D.q + (int64_t)ti.e * D.q_stride + (int64_t)nn * (F / 2) + 16 * hh;
-        srow[j] = D.s + (int64_t)ti.e * D.s_stride + (int64_t)nn * ng;
+        src.q[j] = make_rsrc(D.q + (int64_t)ti.e * D.q_stride, (int64_t)H * (F / 2));
+        src.s[j] = make_rsrc(D.s + (int64_t)ti.e * D.s_stride, (int64_t)H * ng * 4);
+        src.qoff[j] = (uint32_t)(nn * (F / 2) + 16 * hh);
+        src.soff[j] = (uint32_t)(nn * ng * 4);
     }
 
-    Frags<2> fr;
-    mfma_mainloop<2>(fr, arow, brow, srow, ng, s0, s1, s2, s3);
+    Frags<MF> fr;
+    run_mainloop<MF>(fr, src, ng, ti.rows, s0, s1, s2, s3);
 
-    const bool routed = r.wl.pairs != nullptr;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < MF; i++) {
 #pragma unroll
         for (int v = 0; v < 16; v++) {
             const int m = acc_row(i, v, lane);
             if (m < ti.rows) {
                 const int pos = ti.pos0 + m;
-                const float wgt = routed ? r.topk_w[r.wl.pairs[pos]] : 1.0f;
+                const float wgt = sW[m];
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int j = 0; j < NF; j++)
                     if (ncol[j] < H) y[(int64_t)pos * H + ncol[j]] = wgt * fr.acc[i][j][v];
             }
         }
@@ -427,18 +538,20 @@ hipError_t launch_xprep(const uint16_t *x, int tokens, int hidden, uint16_t *x16
 hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *x16,
                               const float *xinv, uint16_t *h16, const MfmaRoute &r,
                               hipStream_t st) {
-    const int ntiles = r.wl.pairs ? r.max_tiles : (r.ntok + BM - 1) / BM;
-    const dim3 grid(xcd_grid((int64_t)ntiles * ((gate.rows + 127) / 128)));
-    hipLaunchKernelGGL(mfma_gateup_kernel, grid, dim3(MF_THREADS), 0, st, gate, up, x16, xinv,
-                       h16, r);
+    constexpr int BMK = GATEUP_BM;
+    const int64_t items = r.wl.pairs ? (int64_t)r.max_tiles * (BM / BMK) : (r.ntok + BMK - 1) / BMK;
+    const dim3 grid(xcd_grid(items * ((gate.rows + 127) / 128)));
+    hipLaunchKernelGGL(mfma_gateup_kernel<BMK>, grid, dim3(MF_THREADS), 0, st, gate, up, x16,
+                       xinv, h16, r);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y, const MfmaRoute &r,
                             hipStream_t st) {
-    const int ntiles = r.wl.pairs ? r.max_tiles : (r.ntok + BM - 1) / BM;
-    const dim3 grid(xcd_grid((int64_t)ntiles * ((down.rows + 255) / 256)));
-    hipLaunchKernelGGL(mfma_down_kernel, grid, dim3(MF_THREADS), 0, st, down, h16, y, r);
+    constexpr int BMK = DOWN_BM;
+    const int64_t items = r.wl.pairs ? (int64_t)r.max_tiles * (BM / BMK) : (r.ntok + BMK - 1) / BMK;
+    const dim3 grid(xcd_grid(items * ((down.rows + 255) / 256)));
+    hipLaunchKernelGGL(mfma_down_kernel<BMK>, grid, dim3(MF_THREADS), 0, st, down, h16, y, r);
     return hipGetLastError();
 }
 

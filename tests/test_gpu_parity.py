@@ -130,7 +130,8 @@ def test_matvec_random(rows, cols, batch, seed):
 # ------------------------------------------------------------ expert ffn ---
 
 @pytest.mark.parametrize("H,F,batch,dtype", [(4096, 1536, 1, "f32"), (4096, 1536, 1, "bf16"),
-                                             (256, 128, 5, "f32"), (256, 128, 130, "bf16")])
+                                             (256, 128, 5, "f32"), (256, 128, 130, "bf16"),
+                                             (256, 128, 600, "bf16")])
 def test_expert_ffn(H, F, batch, dtype):
     say(f"expert ffn H={H} F={F} batch={batch} {dtype}")
     L = Layer(1, H, F, seed=1)
@@ -172,6 +173,18 @@ def test_layer_small_full(dtype, T, k):
     err = rel_l2(out, ref)
     say(f"  rel_l2 = {err:.3e}")
     assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("T,k", [(777, 2), (1500, 1)])
+def test_layer_bf16_multi_tile(T, k):
+    # Few experts and many tokens: each expert spans several 256-row tiles
+    # plus a ragged tail that ends inside a 32-row fragment.
+    say(f"layer multi-tile E=4 H=256 F=128 T={T} k={k} bf16")
+    L = Layer(4, 256, 128, seed=24)
+    out, ref = _layer_case(L, T, k, "bf16", seed=T)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= BF16_TOL
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
