@@ -27,6 +27,15 @@ namespace qmoe {
 
 constexpr int GV_THREADS = 256;
 
+// Blocks per CU the register allocation targets (more waves in flight hide
+// more HBM latency); chosen per shape so that no instance spills.
+template <int GPL, int LPR, int TB, bool DOWN>
+constexpr int gv_occ() {
+    if (GPL != 1 || TB != 1) return 2;
+    if (DOWN) return LPR <= 32 ? 4 : 2;
+    return 3;
+}
+
 template <int GPL>
 struct XReg {
     uint32_t d[GPL][2 * XD_DWORDS];   // two chunks per group
@@ -85,33 +94,76 @@ struct WReg {
     float s[U][GPL];
 };
 
-// Load U rows (row pointers already offset to the expert) for the lane's
-// groups; rows >= nrows or groups >= ng load zeros.
+// One expert's matrix as buffer descriptors (base and byte size in scalar
+// registers) plus this lane's byte offsets inside a row: its groups' 32
+// packed bytes and scales.  A lane without a group gets offsets past the end
+// of the buffer, which read as zero.
+template <int GPL>
+struct RowSrc {
+    __amdgpu_buffer_rsrc_t q, s;
+    uint32_t qlane[GPL], slane[GPL];
+    uint32_t rb, sb;     // packed bytes and scale bytes per row
+};
+
+constexpr uint32_t OOB_OFFSET = 0x80000000u;   // > any descriptor size used here
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(uint32_t)bytes, 0x00020000);
+}
+
+template <int GPL, int LPR>
+__device__ __forceinline__ RowSrc<GPL> row_src(const QMat &M, int e, int lr) {
+    RowSrc<GPL> r;
+    const int ng = M.cols / 64;
+    r.rb = (uint32_t)(M.cols / 2);
+    r.sb = (uint32_t)ng * 4;
+    r.q = gv_rsrc(M.q + (int64_t)e * M.q_stride, (int64_t)M.rows * r.rb);
+    r.s = gv_rsrc(M.s + (int64_t)e * M.s_stride, (int64_t)M.rows * r.sb);
+#pragma unroll
+    for (int gi = 0; gi < GPL; gi++) {
+        const int g = lr + gi * LPR;
+        r.qlane[gi] = g < ng ? (uint32_t)g * 32 : OOB_OFFSET;
+        r.slane[gi] = g < ng ? (uint32_t)g * 4 : OOB_OFFSET;
+    }
+    return r;
+}
+
+// Load U rows (valid row indices) for the lane's groups.  When a lane group
+// is a whole wave the row is wave-uniform and its byte offset goes into the
+// scalar offset operand; otherwise it is added to the lane offset (an
+// out-of-range lane offset stays out of range: rows are < 2^31 bytes).
 template <int GPL, int LPR, int U>
-__device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const uint8_t *const *rowq,
-                                          const float *const *rows, int ng, int lr) {
+__device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const RowSrc<GPL> &src,
+                                          const int *row) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
+        const uint32_t qrow = (uint32_t)row[u] * src.rb;
+        const uint32_t srow = (uint32_t)row[u] * src.sb;
 #pragma unroll
         for (int gi = 0; gi < GPL; gi++) {
-            const int g = lr + gi * LPR;
-            if (rowq[u] != nullptr && g < ng) {
-                const u32x4 *src = (const u32x4 *)(rowq[u] + (int64_t)g * 32);
-                const u32x4 a = src[0], b = src[1];
-                wr.w[u][gi][0] = a.x ^ 0x88888888u;
-                wr.w[u][gi][1] = a.y ^ 0x88888888u;
-                wr.w[u][gi][2] = a.z ^ 0x88888888u;
-                wr.w[u][gi][3] = a.w ^ 0x88888888u;
-                wr.w[u][gi][4] = b.x ^ 0x88888888u;
-                wr.w[u][gi][5] = b.y ^ 0x88888888u;
-                wr.w[u][gi][6] = b.z ^ 0x88888888u;
-                wr.w[u][gi][7] = b.w ^ 0x88888888u;
-                wr.s[u][gi] = rows[u][g];
+            u32x4 a, b;
+            float sc;
+            if (LPR == 64) {
+                a = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi], qrow, 0);
+                b = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + 16, qrow, 0);
+                sc = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(src.s, src.slane[gi], srow, 0));
             } else {
-#pragma unroll
-                for (int d = 0; d < 8; d++) wr.w[u][gi][d] = 0;
-                wr.s[u][gi] = 0.f;
+                a = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + qrow, 0, 0);
+                b = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + qrow + 16, 0, 0);
+                sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                   src.s, src.slane[gi] + srow, 0, 0));
             }
+            wr.w[u][gi][0] = a.x ^ 0x88888888u;
+            wr.w[u][gi][1] = a.y ^ 0x88888888u;
+            wr.w[u][gi][2] = a.z ^ 0x88888888u;
+            wr.w[u][gi][3] = a.w ^ 0x88888888u;
+            wr.w[u][gi][4] = b.x ^ 0x88888888u;
+            wr.w[u][gi][5] = b.y ^ 0x88888888u;
+            wr.w[u][gi][6] = b.z ^ 0x88888888u;
+            wr.w[u][gi][7] = b.w ^ 0x88888888u;
+            wr.s[u][gi] = sc;
         }
     }
 }
@@ -175,22 +227,22 @@ constexpr int batch_rows() {
     return (4 / GPL) < NSTEP ? (4 / GPL < 1 ? 1 : 4 / GPL) : NSTEP;
 }
 
-// Stream NSTEP rows per lane group (LPR lanes) in batches of U rows, the
-// next batch's loads issued before the current batch is computed.
-// row_at(step, q, s) gives the packed row and its scales (q == nullptr:
-// no row); emit(step, j, value) runs on the last lane of the group.
+// Stream NSTEP rows per lane group (LPR lanes) of matrix `src` in batches of
+// U rows, the next batch's loads issued before the current batch is
+// computed.  row_at(step) gives the (valid) row index; emit(step, j, value)
+// runs on the last lane of the group.
 template <int GPL, int LPR, int TB, int U, int NSTEP, class RowAt, class Prologue, class Emit>
-__device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int ng, int lr,
-                                            RowAt row_at, Prologue prologue, Emit emit) {
+__device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
+                                            const RowSrc<GPL> &src, RowAt row_at,
+                                            Prologue prologue, Emit emit) {
     constexpr int NB = NSTEP / U;
     static_assert(NB * U == NSTEP, "NSTEP must be a multiple of U");
     WReg<GPL, U> w[2];
     auto load_batch = [&](int b, WReg<GPL, U> &dst) {
-        const uint8_t *rq[U];
-        const float *rs[U];
+        int rows[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) row_at(b * U + u, rq[u], rs[u]);
-        load_rows<GPL, LPR, U>(dst, rq, rs, ng, lr);
+        for (int u = 0; u < U; u++) rows[u] = row_at(b * U + u);
+        load_rows<GPL, LPR, U>(dst, src, rows);
     };
     // The first weight batch depends only on the expert; issue it before the
     // prologue's dependent chain (pair -> token -> activation digits).
@@ -219,7 +271,7 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int ng,
 // one digit chunk per sorted position.
 // ---------------------------------------------------------------------------
 template <int GPL, int LPR, int TB>
-__global__ void __launch_bounds__(GV_THREADS) gemv_gateup_kernel(QMat G, QMat Up, XDigits xd,
+__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false>())) gemv_gateup_kernel(QMat G, QMat Up, XDigits xd,
                                                                  XDigits hd, GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;       // lane groups per block
     constexpr int NR = 64;                     // row tasks per block
@@ -233,23 +285,19 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_gateup_kernel(QMat G, QMat Up
     const int ng = H / 64, ncx = H / XD_CHUNK, nch = F / XD_CHUNK;
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
     const int row0 = blockIdx.x * 32;
-    const int64_t rb = H / 2;
-    const uint8_t *gq = G.q + (int64_t)e * G.q_stride;
-    const uint8_t *uq = Up.q + (int64_t)e * Up.q_stride;
-    const float *gs = G.s + (int64_t)e * G.s_stride;
-    const float *us = Up.s + (int64_t)e * Up.s_stride;
-    auto row_at = [&](int step, const uint8_t *&q, const float *&s) {
-        const int ri = slot * NSTEP + step;       // 0..63: gate rows, then up rows
-        const int o = row0 + (ri & 31);
-        q = (ri < 32 ? gq : uq) + (int64_t)o * rb;
-        s = (ri < 32 ? gs : us) + (int64_t)o * ng;
-    };
+    // Row tasks 0..63 are the 32 gate rows then the same 32 up rows; every
+    // wave owns 16 consecutive tasks (NSTEP rows for each of its 64/LPR lane
+    // groups), so waves 0-1 read gate and waves 2-3 up.
+    static_assert(NSTEP * (64 / LPR) == 16, "16 row tasks per wave");
+    const bool up_wave = __builtin_amdgcn_readfirstlane(wave_id()) >= 2;
+    const RowSrc<GPL> src = row_src<GPL, LPR>(up_wave ? Up : G, e, lr);
+    auto row_at = [&](int step) { return row0 + ((slot * NSTEP + step) & 31); };
 
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
         XReg<GPL> xr[TB];
         stream_rows<GPL, LPR, TB, U, NSTEP>(
-            xr, nt, ng, lr, row_at,
+            xr, nt, lr, src, row_at,
             [&]() {
 #pragma unroll
                 for (int j = 0; j < TB; j++)
@@ -278,7 +326,7 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_gateup_kernel(QMat G, QMat Up
 // the preparation kernel); direct mode stores y to out[pos].
 // ---------------------------------------------------------------------------
 template <int GPL, int LPR, int TB>
-__global__ void __launch_bounds__(GV_THREADS) gemv_down_kernel(QMat D, XDigits hd,
+__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true>())) gemv_down_kernel(QMat D, XDigits hd,
                                                                float *__restrict__ out,
                                                                GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;
@@ -292,15 +340,10 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_down_kernel(QMat D, XDigits h
     const int ng = I / 64, ncx = I / XD_CHUNK;
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
     const int row0 = blockIdx.x * NR + slot * NSTEP;
-    const int64_t rbytes = I / 2;
-    const uint8_t *dq = D.q + (int64_t)e * D.q_stride;
-    const float *ds = D.s + (int64_t)e * D.s_stride;
     const bool routed = r.rec != nullptr;
-    auto row_at = [&](int step, const uint8_t *&q, const float *&s) {
-        const int o = row0 + step;
-        q = o < O ? dq + (int64_t)o * rbytes : nullptr;
-        s = ds + (int64_t)(o < O ? o : 0) * ng;
-    };
+    const RowSrc<GPL> src = row_src<GPL, LPR>(D, e, lr);
+    // rows past O re-read row O-1 and are never emitted
+    auto row_at = [&](int step) { return min(row0 + step, O - 1); };
 
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
@@ -324,7 +367,7 @@ __global__ void __launch_bounds__(GV_THREADS) gemv_down_kernel(QMat D, XDigits h
                 }
             }
         };
-        stream_rows<GPL, LPR, TB, U, NSTEP>(xr, nt, ng, lr, row_at, prologue,
+        stream_rows<GPL, LPR, TB, U, NSTEP>(xr, nt, lr, src, row_at, prologue,
                                             [&](int step, int j, float v) {
                                                 const int o = row0 + step;
                                                 if (o < O) {
