@@ -11,8 +11,9 @@ floating input is widened exactly to float64 before the call (f32 and bf16
 are exact in double), so the oracle sees the same numbers the GPU sees.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_*``):
-pack/unpack, matvec, pair, silu, ffn, worklist and layer are all pinned by
-hand-written values, closed forms or brute force; none is "parity unpinned".
+pack/unpack, matvec, pair, silu, ffn, worklist, layer and route are all
+pinned by hand-written values, closed forms or brute force; none is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -78,6 +79,8 @@ def load(path=None):
     lib.orc_layer.restype = i64
     lib.orc_layer.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
                               i64, vp, vp, i64, vp]
+    lib.orc_route.restype = None
+    lib.orc_route.argtypes = [vp, i64, i64, i64, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -210,3 +213,12 @@ class Oracle:
                                  _p(sd), experts, hidden, inter, gs, _p(x),
                                  tokens, _p(ids), _p(w), k, _p(out))
         return out, int(bad)
+
+    def route(self, logits, k):
+        """Top-k ids (pick order) and f32 softmax weights over the picked."""
+        logits = _c(_np(logits), np.float32)
+        tokens, experts = logits.shape
+        ids = np.empty((tokens, k), np.int32)
+        w = np.empty((tokens, k), np.float32)
+        self.lib.orc_route(_p(logits), tokens, experts, k, _p(ids), _p(w))
+        return ids, w

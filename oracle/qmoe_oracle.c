@@ -29,6 +29,9 @@
  *  - pxq_llama.cpp release notes, section "Device-side MoE row map": the
  *    token-to-expert table (histogram, scan, fill) for one batched MoE
  *    layer.
+ *  - the same pull request, the quoted issue's list of CPU work: the
+ *    router's top-K picks with one "taken" flag per expert, K passes over
+ *    the E logits.
  *
  * Readings taken where the pages are silent (each listed with its reason in
  * the design notes of this repository):
@@ -38,7 +41,10 @@
  *  - SiLU(z) = z / (1 + exp(-z)); expert FFN = down(silu(gate x) * (up x));
  *  - layer output = sum over the k routing slots, in slot order, of
  *    weight * expert_ffn(x); ids outside [0, E) are dropped and counted;
- *  - worklist = stable counting sort of pair p = t*K + k by expert id.
+ *  - worklist = stable counting sort of pair p = t*K + k by expert id;
+ *  - router: each pass picks the untaken expert with the largest logit, the
+ *    lowest id among equal logits, NaN ranking as -infinity; slot order is
+ *    pick order; weights are the softmax over the K picked logits.
  */
 #include <math.h>
 #include <stddef.h>
@@ -210,4 +216,45 @@ int64_t orc_layer(const uint8_t *pg, const float *sg, const uint8_t *pu,
     }
     free(y);
     return bad;
+}
+
+/* ---- router (the step ahead of the path) ---------------------------------
+ * Top-K with a taken flag per expert: K passes, each scanning the E logits
+ * of the token upward and keeping the untaken expert whose logit is
+ * strictly larger than the best so far (so equal logits go to the lowest
+ * id); NaN ranks as -infinity.  Slot s holds the s-th pick.  Weight of slot
+ * s = exp(l_s - l_0) / sum_j exp(l_j - l_0) over the K picked logits (l_0 is
+ * the largest), in double, rounded once to f32.  Non-finite logits make the
+ * weights non-finite; the picks stay defined. */
+void orc_route(const float *logits, int64_t tokens, int64_t experts, int64_t k,
+               int32_t *ids, float *w) {
+    unsigned char *taken = (unsigned char *)malloc((size_t)experts);
+    double *ex = (double *)malloc(sizeof(double) * (size_t)k);
+    for (int64_t t = 0; t < tokens; t++) {
+        const float *l = logits + t * experts;
+        for (int64_t e = 0; e < experts; e++) taken[e] = 0;
+        for (int64_t s = 0; s < k; s++) {
+            int64_t best = -1;
+            double best_key = 0.0;
+            for (int64_t e = 0; e < experts; e++) {
+                if (taken[e]) continue;
+                double key = isnan(l[e]) ? -INFINITY : (double)l[e];
+                if (best < 0 || key > best_key) {
+                    best = e;
+                    best_key = key;
+                }
+            }
+            taken[best] = 1;
+            ids[t * k + s] = (int32_t)best;
+        }
+        double top = (double)l[ids[t * k]];
+        double sum = 0.0;
+        for (int64_t s = 0; s < k; s++) {
+            ex[s] = exp((double)l[ids[t * k + s]] - top);
+            sum += ex[s];
+        }
+        for (int64_t s = 0; s < k; s++) w[t * k + s] = (float)(ex[s] / sum);
+    }
+    free(ex);
+    free(taken);
 }

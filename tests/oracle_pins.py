@@ -11,6 +11,8 @@ gs=64) support + diagnostic harness" (Summary; comments "implementation
 complete but system-instability", "blocked by GPU driver instability",
 "Here's the oracle you're missing", "fmt=4 CUDA attention crash - root cause,
 fix"), and the pxq_llama.cpp release notes, section "Device-side MoE row map".
+The router pins follow the same pull request's quoted issue (list of CPU
+work: router top-K with a taken flag per expert).
 """
 from __future__ import annotations
 
@@ -432,6 +434,65 @@ def pin_layer_invalid_ids(orc):
                            np.array([[0.5, 9.0, 0.25, 7.0]], np.float32))
     assert bad == 2
     assert np.array_equal(good, mixed)
+
+
+
+# ---------------------------------------------------------------- router ---
+
+def _route_case_logits(case):
+    return np.array([[float(v) for v in row] for row in case["logits"]], dtype=np.float32)
+
+
+def pin_route_hand(orc):
+    """Hand-evaluated picks and weights (ties, NaN / -inf ranking, k = 1)."""
+    for case in _golden("hand_cases.json")["route"]:
+        ids, w = orc.route(_route_case_logits(case), case["k"])
+        assert ids.tolist() == case["ids"], (case["name"], ids.tolist())
+        if "w" in case:
+            _close(w, case["w"], rtol=1e-7, what=case["name"])
+
+
+def pin_route_sort_and_softmax_library(orc):
+    """Distinct logits: the picks are numpy's descending argsort, the weights
+    scipy's softmax over the picked logits (library routines)."""
+    from scipy.special import softmax
+    rng = _rng(40)
+    for (T, E, k) in [(5, 16, 4), (3, 128, 8), (2, 7, 7), (4, 256, 8)]:
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        ids, w = orc.route(logits, k)
+        ref_ids = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref_ids)
+        picked = np.take_along_axis(logits.astype(np.float64), ref_ids, axis=1)
+        ref_w = softmax(picked, axis=1).astype(np.float32)
+        _close(w, ref_w, rtol=2e-7, what="softmax")
+
+
+def pin_route_all_equal(orc):
+    """All logits equal: ids 0..k-1 in order, every weight 1/k."""
+    logits = np.full((3, 12), 0.75, dtype=np.float32)
+    for k in (1, 4, 12):
+        ids, w = orc.route(logits, k)
+        assert ids.tolist() == [list(range(k))] * 3
+        _close(w, np.full((3, k), 1.0 / k), rtol=1e-7, what="uniform")
+
+
+def pin_route_shift_invariant(orc):
+    """Adding a constant to a token's logits changes neither picks nor weights
+    (beyond the f32 rounding of the shifted logits)."""
+    rng = _rng(41)
+    logits = (rng.standard_normal((6, 64)) * 2).astype(np.float32)
+    ids0, w0 = orc.route(logits, 8)
+    ids1, w1 = orc.route(logits + np.float32(16.0), 8)
+    assert np.array_equal(ids0, ids1)
+    _close(w1, w0, rtol=2e-5, what="shift")
+
+
+def pin_route_weights_sum_to_one(orc):
+    rng = _rng(42)
+    logits = (rng.standard_normal((32, 128)) * 3).astype(np.float32)
+    _, w = orc.route(logits, 8)
+    _close(w.astype(np.float64).sum(axis=1), np.ones(32), rtol=1e-6, what="sum")
+    assert np.all(np.diff(w, axis=1) <= 0), "slot order is descending logit"
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -38,6 +38,15 @@ MUTANTS = [
     ("worklist_invalid_not_counted", "if (e < 0 || e >= experts) bad++;\n        else counts[e]++;",
      "if (e < 0 || e >= experts) {}\n        else counts[e]++;"),
     ("pack_bad_not_counted", "if (v0 < -8 || v0 > 7) bad++;", "(void)0;"),
+    ("route_ties_to_highest_id", "if (best < 0 || key > best_key) {",
+     "if (best < 0 || key >= best_key) {"),
+    ("route_taken_flag_not_set", "taken[best] = 1;", "(void)taken;"),
+    ("route_softmax_over_first_experts", "ex[s] = exp((double)l[ids[t * k + s]] - top);",
+     "ex[s] = exp((double)l[s] - top);"),
+    ("route_nan_not_demoted", "double key = isnan(l[e]) ? -INFINITY : (double)l[e];",
+     "double key = (double)l[e];"),
+    ("route_weights_not_normalised", "w[t * k + s] = (float)(ex[s] / sum);",
+     "w[t * k + s] = (float)ex[s];"),
 ]
 
 
