@@ -147,6 +147,41 @@ def cpu_baseline(qm, synth, oracle, layers_codes, layers_scales, decode_inputs, 
         host_cpus=os.cpu_count())
 
 
+def time_router(qm, synth, torch, dev, reps=20):
+    """The device router (top-k + softmax over the picked logits), the step
+    ahead of the layer, timed on its own with HIP events on the current
+    stream; not part of the step.  Algorithmic bytes: logits in, ids and
+    weights out."""
+    res = {}
+    for name, wl_name, T in (("t8192_e128_uniform", "prefill_e128_t8192", PREFILL_T),
+                             ("t16_e128_normal", "decode_e128_t16", 16)):
+        wl = synth.LAYERS[wl_name]
+        logits = synth.make_logits(wl, synth.generator(wl.seed + 1000), T).to(dev)
+        ids = torch.empty(T, K, dtype=torch.int32, device=dev)
+        w = torch.empty(T, K, dtype=torch.float32, device=dev)
+        # captured in a HIP graph: a few-microsecond kernel is shorter than
+        # issuing it from Python
+        qm.qmoe_route(logits, K, ids, w)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            for _ in range(reps):
+                qm.qmoe_route(logits, K, ids, w)
+        graph.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        nbytes = T * E * 4 + T * K * 8
+        res[name] = {"us": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_roofline": round(nbytes / HBM_PEAK / (us * 1e-6), 4),
+                     "alg_bytes": nbytes}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,6 +393,7 @@ def main():
             "avg_launch_ms": round(gateup_ms, 4),
         },
     }
+    rec["router"] = time_router(qm, synth, torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         log("timing the CPU oracle on a bounded sample ...")

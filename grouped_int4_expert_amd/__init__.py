@@ -58,7 +58,7 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_pack", "qmoe_unpack", "qmoe_matvec_workspace_bytes", "qmoe_matvec",
            "qmoe_expert_ffn_workspace_bytes", "qmoe_expert_ffn",
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
-           "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout"]
+           "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route"]
 
 _lib = None
 
@@ -96,6 +96,7 @@ def load(path: str | None = None):
                                          i32]),
         "qmoe_layer_ws_layout": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32,
                                                 ctypes.POINTER(qmoe_layer_ws_view)]),
+        "qmoe_route": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -306,6 +307,19 @@ def qmoe_worklist(topk_ids, experts, ws=None, stream=None):
     out["pairs"] = out["pairs"][:n]
     out["inv"] = out["inv"][:n]
     return out
+
+
+def qmoe_route(logits, k, ids=None, w=None, stream=None):
+    """Device router: top-k ids (pick order) and softmax weights over the
+    picked logits, for f32 logits [T, E]."""
+    _dev(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    ids = ids if ids is not None else torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = w if w is not None else torch.empty(T, k, dtype=torch.float32, device=dev)
+    _check(load().qmoe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)),
+           "qmoe_route")
+    return ids, w
 
 
 def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=None):

@@ -327,6 +327,22 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     return status_of(e);
 }
 
+int qmoe_route(const float *logits, int32_t tokens, int32_t experts, int32_t k,
+               int32_t *topk_ids, float *topk_w, void *stream) {
+    if (tokens < 0 || experts < 1 || k < 1 || k > experts) return QMOE_ERR_SHAPE;
+    if ((int64_t)tokens * experts > (int64_t)1 << 31) return QMOE_ERR_SHAPE;
+    if (!route_supported(experts, k)) return QMOE_ERR_UNSUPPORTED;
+    if (tokens == 0) return QMOE_OK;
+    if (!logits || !topk_ids || !topk_w) return QMOE_ERR_NULL;
+    if (!aligned4(logits) || !aligned4(topk_ids) || !aligned4(topk_w)) return QMOE_ERR_ALIGN;
+    const int64_t nl = 4 * (int64_t)tokens * experts, no = 4 * (int64_t)tokens * k;
+    if (overlap(topk_ids, no, logits, nl) || overlap(topk_w, no, logits, nl) ||
+        overlap(topk_ids, no, topk_w, no))
+        return QMOE_ERR_ALIAS;
+    return status_of(launch_route(logits, tokens, experts, k, topk_ids, topk_w,
+                                  as_stream(stream)));
+}
+
 size_t qmoe_worklist_workspace_bytes(int32_t tokens, int32_t k, int32_t experts) {
     if (tokens < 0 || k < 1 || experts < 1) return 0;
     return (size_t)(4 * wl_scratch_ints((int64_t)tokens * k, experts));

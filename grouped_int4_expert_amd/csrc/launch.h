@@ -115,4 +115,11 @@ hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y,
 hipError_t launch_combine(const float *y, const int32_t *inv, int tokens, int k, int hidden,
                           float *out, hipStream_t st);
 
+// Router: ids [tokens][k] (pick order) and softmax weights over the picked
+// logits, one wave per token.
+constexpr int MAX_ROUTE_TOPK = 16;
+bool route_supported(int experts, int k);
+hipError_t launch_route(const float *logits, int tokens, int experts, int k, int32_t *ids,
+                        float *w, hipStream_t st);
+
 }  // namespace qmoe

@@ -174,6 +174,24 @@ int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k,
                   int32_t *pairs, int32_t *inv, int32_t *n_invalid, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* Router, the step ahead of the layer: for each token, the k experts with
+ * the largest logits and their routing weights (colibri pull request
+ * "cuda+engine: full fmt=4 (grouped int4 gs=64) support", the quoted issue's
+ * list of CPU work: top-K with one taken flag per expert).  k passes, each
+ * picking the untaken expert with the largest logit, the lowest id among
+ * equal logits, NaN ranking as -infinity.  Inputs: logits f32 [tokens]
+ * [experts] (device, 4-byte aligned).  Outputs (device, 4-byte aligned):
+ * topk_ids int32 [tokens][k] in pick order (unique per token, bit-exact
+ * against any correct implementation) and topk_w f32 [tokens][k] =
+ * exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k picked logits (f32
+ * arithmetic; non-finite logits give non-finite weights).  The outputs feed
+ * qmoe_layer unchanged on the same stream, with no host round trip.
+ * Limits: 1 <= k <= min(experts, 16), experts <= 1024 (else
+ * QMOE_ERR_UNSUPPORTED); outputs may not overlap the logits or each other
+ * (QMOE_ERR_ALIAS).  tokens == 0 launches nothing. */
+int qmoe_route(const float *logits, int32_t tokens, int32_t experts, int32_t k,
+               int32_t *topk_ids, float *topk_w, void *stream);
+
 /* Workspace bytes qmoe_layer needs for these sizes and dtype. */
 size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
                                   int32_t k, int32_t x_dtype);

@@ -157,3 +157,19 @@ def test_expert_ffn_rejections(lib):
     D2 = qmat(256, 192)
     assert lib.qmoe_expert_ffn(ctypes.byref(G), ctypes.byref(U), ctypes.byref(D2), 0, FAKE, 2,
                                FAKE + (30 << 32), ws, nb, None) == 2
+
+
+def test_route_rejections(lib):
+    L, I, W = FAKE, FAKE + (50 << 32), FAKE + (51 << 32)
+    assert lib.qmoe_route(L, 4, 128, 0, I, W, None) == 2          # k < 1
+    assert lib.qmoe_route(L, 4, 8, 9, I, W, None) == 2            # k > experts
+    assert lib.qmoe_route(L, -1, 128, 8, I, W, None) == 2         # tokens < 0
+    assert lib.qmoe_route(L, 4, 0, 1, I, W, None) == 2            # no experts
+    assert lib.qmoe_route(L, 4, 128, 17, I, W, None) == 4         # k beyond 16
+    assert lib.qmoe_route(L, 4, 2048, 8, I, W, None) == 4         # experts beyond 1024
+    assert lib.qmoe_route(None, 4, 128, 8, I, W, None) == 1
+    assert lib.qmoe_route(L, 4, 128, 8, None, W, None) == 1
+    assert lib.qmoe_route(L + 2, 4, 128, 8, I, W, None) == 3      # misaligned logits
+    assert lib.qmoe_route(L, 4, 128, 8, L + 64, W, None) == 6     # ids inside the logits
+    assert lib.qmoe_route(L, 4, 128, 8, I, I + 16, None) == 6     # ids and weights overlap
+    assert lib.qmoe_route(L, 0, 128, 8, None, None, None) == 0    # nothing to do
