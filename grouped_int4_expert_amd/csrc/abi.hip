@@ -34,25 +34,34 @@ inline int status_of(hipError_t e) { return e == hipSuccess ? QMOE_OK : QMOE_ERR
 // through buffer descriptors with 32-bit byte sizes and offsets.
 inline bool mfma_fits(int64_t H, int64_t F, int64_t x_rows, int64_t h_rows) {
     const int64_t lim = (int64_t)1 << 32;
-    return x_rows * H * 2 < lim && h_rows * F * 2 < lim && H * F / 2 < lim && H * F / 16 < lim;
+    return x_rows * H * 2 < lim && h_rows * F * 2 < lim && H * F / 2 < lim && H * F / 8 < lim;
 }
 
 int64_t packed_bytes(int64_t rows, int64_t cols) { return rows * ((cols + 1) / 2); }
 int64_t scale_count(int64_t rows, int64_t cols, int64_t g) { return rows * ((cols + g - 1) / g); }
 
-// Validate one matrix descriptor for the GPU kernels: expected shape,
-// group 64, cols % 64 == 0, aligned pointers and expert strides.
+// Group sizes the GPU kernels take for a row of `cols` inputs: 32, 64 times a
+// power of two (64, 128, 256, ...), or at least the row (one scale per row).
+bool group_supported(int group, int cols) {
+    if (group == 32 || group >= cols) return group > 0;
+    if (group % 64 != 0) return false;
+    const int m = group / 64;
+    return (m & (m - 1)) == 0;
+}
+
+// Validate one matrix descriptor for the GPU kernels: expected shape, a
+// supported group, cols % 64 == 0, aligned pointers and expert strides.
 int check_qmat(const qmoe_qmat *m, int rows, int cols, int experts) {
     if (!m) return QMOE_ERR_NULL;
     if (m->struct_size != sizeof(qmoe_qmat)) return QMOE_ERR_ABI;
     if (m->rows != rows || m->cols != cols || rows <= 0 || cols <= 0) return QMOE_ERR_SHAPE;
     if (m->group <= 0) return QMOE_ERR_SHAPE;
-    if (m->group != 64 || cols % 64 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (!group_supported(m->group, cols) || cols % 64 != 0) return QMOE_ERR_UNSUPPORTED;
     if (!m->q || !m->s) return QMOE_ERR_NULL;
     if (!aligned16(m->q) || !aligned16(m->s)) return QMOE_ERR_ALIGN;
     if (experts > 1) {
         if (m->q_expert_stride < packed_bytes(rows, cols) ||
-            m->s_expert_stride < scale_count(rows, cols, 64))
+            m->s_expert_stride < scale_count(rows, cols, m->group))
             return QMOE_ERR_SHAPE;
         if (m->q_expert_stride % 16 != 0 || m->s_expert_stride % 4 != 0) return QMOE_ERR_ALIGN;
     }
@@ -67,6 +76,7 @@ QMat to_qmat(const qmoe_qmat *m) {
     q.s_stride = m->s_expert_stride;
     q.rows = m->rows;
     q.cols = m->cols;
+    q.group = m->group;
     return q;
 }
 
@@ -149,7 +159,9 @@ int check_layer_desc(const qmoe_layer_desc *d) {
     if (d->experts < 1 || d->experts > MAX_EXPERTS || d->hidden <= 0 || d->inter <= 0)
         return QMOE_ERR_SHAPE;
     if (d->group <= 0) return QMOE_ERR_SHAPE;
-    if (d->group != 64 || d->hidden % 64 || d->inter % 64) return QMOE_ERR_UNSUPPORTED;
+    if (d->hidden % 64 || d->inter % 64) return QMOE_ERR_UNSUPPORTED;
+    if (d->gate.group != d->group || d->up.group != d->group || d->down.group != d->group)
+        return QMOE_ERR_SHAPE;
     int s;
     if ((s = check_qmat(&d->gate, d->inter, d->hidden, d->experts))) return s;
     if ((s = check_qmat(&d->up, d->inter, d->hidden, d->experts))) return s;
@@ -169,7 +181,7 @@ const char *qmoe_status_str(int status) {
         case QMOE_ERR_NULL: return "null pointer";
         case QMOE_ERR_SHAPE: return "bad shape or size";
         case QMOE_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
-        case QMOE_ERR_UNSUPPORTED: return "unsupported by the GPU kernels (group must be 64, cols % 64 == 0)";
+        case QMOE_ERR_UNSUPPORTED: return "unsupported by the GPU kernels (group 32, 64 * 2^j or a whole row; cols % 64 == 0)";
         case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
         case QMOE_ERR_ALIAS: return "output overlaps an input or the workspace";
         case QMOE_ERR_ABI: return "struct_size mismatch (library and caller built from different headers)";
@@ -234,7 +246,7 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     const int64_t xb = (int64_t)batch * W->cols * 4, yb = (int64_t)batch * W->rows * 4;
     if (overlap(y, yb, x, xb) || overlap(y, yb, ws, need) || overlap(x, xb, ws, need) ||
         overlap(y, yb, W->q, packed_bytes(W->rows, W->cols)) ||
-        overlap(y, yb, W->s, 4 * scale_count(W->rows, W->cols, 64)))
+        overlap(y, yb, W->s, 4 * scale_count(W->rows, W->cols, W->group)))
         return QMOE_ERR_ALIAS;
     Carver c(ws);
     XDigits xd;
@@ -279,6 +291,7 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     if ((s = check_qmat(gate, F, H, 1))) return s;
     if ((s = check_qmat(up, F, H, 1))) return s;
     if ((s = check_qmat(down, H, F, 1))) return s;
+    if (gate->group != up->group) return QMOE_ERR_SHAPE;   // one fused gate+up pass
     if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
     if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
         return QMOE_ERR_UNSUPPORTED;

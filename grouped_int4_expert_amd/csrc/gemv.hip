@@ -29,11 +29,11 @@ constexpr int GV_THREADS = 256;
 
 // Blocks per CU the register allocation targets (more waves in flight hide
 // more HBM latency); chosen per shape so that no instance spills.
-template <int GPL, int LPR, int TB, bool DOWN>
+template <int GPL, int LPR, int TB, bool DOWN, bool G32>
 constexpr int gv_occ() {
     if (GPL != 1 || TB != 1) return 2;
-    if (DOWN) return LPR <= 32 ? 4 : 2;
-    return 3;
+    if (DOWN) return LPR <= 32 ? (G32 ? 3 : 4) : 2;
+    return G32 ? 2 : 3;
 }
 
 template <int GPL>
@@ -91,13 +91,14 @@ __device__ __forceinline__ float chunk_dot(const uint32_t *w, const uint32_t *x,
 template <int GPL, int U>
 struct WReg {
     uint32_t w[U][GPL][8];
-    float s[U][GPL];
+    float s[U][GPL][2];   // group 32: one scale per 32-input chunk; else [1] unused
 };
 
 // One expert's matrix as buffer descriptors (base and byte size in scalar
-// registers) plus this lane's byte offsets inside a row: its groups' 32
-// packed bytes and scales.  A lane without a group gets offsets past the end
-// of the buffer, which read as zero.
+// registers) plus this lane's byte offsets inside a row: its 64-input
+// groups' 32 packed bytes and their scales (group 32: the two scales of the
+// two chunks; group 64m: scale (64 g) / group).  A lane without a group gets
+// offsets past the end of the buffer, which read as zero.
 template <int GPL>
 struct RowSrc {
     __amdgpu_buffer_rsrc_t q, s;
@@ -112,19 +113,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int6
                                              (int)(uint32_t)bytes, 0x00020000);
 }
 
-template <int GPL, int LPR>
+template <int GPL, int LPR, bool G32>
 __device__ __forceinline__ RowSrc<GPL> row_src(const QMat &M, int e, int lr) {
     RowSrc<GPL> r;
     const int ng = M.cols / 64;
     r.rb = (uint32_t)(M.cols / 2);
-    r.sb = (uint32_t)ng * 4;
+    r.sb = (uint32_t)scales_per_row(M) * 4;
     r.q = gv_rsrc(M.q + (int64_t)e * M.q_stride, (int64_t)M.rows * r.rb);
     r.s = gv_rsrc(M.s + (int64_t)e * M.s_stride, (int64_t)M.rows * r.sb);
 #pragma unroll
     for (int gi = 0; gi < GPL; gi++) {
         const int g = lr + gi * LPR;
+        const uint32_t si = G32 ? 2u * g : (uint32_t)(g * 64 / M.group);
         r.qlane[gi] = g < ng ? (uint32_t)g * 32 : OOB_OFFSET;
-        r.slane[gi] = g < ng ? (uint32_t)g * 4 : OOB_OFFSET;
+        r.slane[gi] = g < ng ? si * 4 : OOB_OFFSET;
     }
     return r;
 }
@@ -133,7 +135,7 @@ __device__ __forceinline__ RowSrc<GPL> row_src(const QMat &M, int e, int lr) {
 // is a whole wave the row is wave-uniform and its byte offset goes into the
 // scalar offset operand; otherwise it is added to the lane offset (an
 // out-of-range lane offset stays out of range: rows are < 2^31 bytes).
-template <int GPL, int LPR, int U>
+template <int GPL, int LPR, int U, bool G32>
 __device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const RowSrc<GPL> &src,
                                           const int *row) {
 #pragma unroll
@@ -143,17 +145,18 @@ __device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const RowSrc<GPL> &s
 #pragma unroll
         for (int gi = 0; gi < GPL; gi++) {
             u32x4 a, b;
-            float sc;
-            if (LPR == 64) {
-                a = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi], qrow, 0);
-                b = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + 16, qrow, 0);
-                sc = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(src.s, src.slane[gi], srow, 0));
+            u32x2 sc;
+            const uint32_t qv = LPR == 64 ? src.qlane[gi] : src.qlane[gi] + qrow;
+            const uint32_t qs = LPR == 64 ? qrow : 0u;
+            const uint32_t sv = LPR == 64 ? src.slane[gi] : src.slane[gi] + srow;
+            const uint32_t ss = LPR == 64 ? srow : 0u;
+            a = __builtin_amdgcn_raw_buffer_load_b128(src.q, qv, qs, 0);
+            b = __builtin_amdgcn_raw_buffer_load_b128(src.q, qv + 16, qs, 0);
+            if (G32) {
+                sc = __builtin_amdgcn_raw_buffer_load_b64(src.s, sv, ss, 0);
             } else {
-                a = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + qrow, 0, 0);
-                b = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane[gi] + qrow + 16, 0, 0);
-                sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                   src.s, src.slane[gi] + srow, 0, 0));
+                sc.x = __builtin_amdgcn_raw_buffer_load_b32(src.s, sv, ss, 0);
+                sc.y = sc.x;
             }
             wr.w[u][gi][0] = a.x ^ 0x88888888u;
             wr.w[u][gi][1] = a.y ^ 0x88888888u;
@@ -163,19 +166,21 @@ __device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const RowSrc<GPL> &s
             wr.w[u][gi][5] = b.y ^ 0x88888888u;
             wr.w[u][gi][6] = b.z ^ 0x88888888u;
             wr.w[u][gi][7] = b.w ^ 0x88888888u;
-            wr.s[u][gi] = sc;
+            wr.s[u][gi][0] = __uint_as_float(sc.x);
+            wr.s[u][gi][1] = __uint_as_float(sc.y);
         }
     }
 }
 
-template <int GPL, int U>
+template <int GPL, int U, bool G32>
 __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XReg<GPL> &xr) {
     float acc = 0.f;
 #pragma unroll
     for (int gi = 0; gi < GPL; gi++) {
         const float g0 = chunk_dot(&wr.w[u][gi][0], &xr.d[gi][0], xr.f[gi][0]);
         const float g1 = chunk_dot(&wr.w[u][gi][4], &xr.d[gi][XD_DWORDS], xr.f[gi][1]);
-        acc = fmaf(wr.s[u][gi], g0 + g1, acc);
+        if (G32) acc = fmaf(wr.s[u][gi][1], g1, fmaf(wr.s[u][gi][0], g0, acc));
+        else acc = fmaf(wr.s[u][gi][0], g0 + g1, acc);
     }
     return acc;
 }
@@ -231,7 +236,8 @@ constexpr int batch_rows() {
 // U rows, the next batch's loads issued before the current batch is
 // computed.  row_at(step) gives the (valid) row index; emit(step, j, value)
 // runs on the last lane of the group.
-template <int GPL, int LPR, int TB, int U, int NSTEP, class RowAt, class Prologue, class Emit>
+template <int GPL, int LPR, int TB, int U, int NSTEP, bool G32, class RowAt, class Prologue,
+          class Emit>
 __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
                                             const RowSrc<GPL> &src, RowAt row_at,
                                             Prologue prologue, Emit emit) {
@@ -242,7 +248,7 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
         int rows[U];
 #pragma unroll
         for (int u = 0; u < U; u++) rows[u] = row_at(b * U + u);
-        load_rows<GPL, LPR, U>(dst, src, rows);
+        load_rows<GPL, LPR, U, G32>(dst, src, rows);
     };
     // The first weight batch depends only on the expert; issue it before the
     // prologue's dependent chain (pair -> token -> activation digits).
@@ -256,7 +262,7 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
             if (j < nt) {
 #pragma unroll
                 for (int u = 0; u < U; u++) {
-                    float v = row_dot<GPL, U>(w[b & 1], u, xr[j]);
+                    float v = row_dot<GPL, U, G32>(w[b & 1], u, xr[j]);
                     v = reduce_dpp<LPR>(v);
                     if (lr == LPR - 1) emit(b * U + u, j, v);
                 }
@@ -270,8 +276,8 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
 // same 32 up rows (64 row tasks).  Writes h = silu(g)*u for the 32 rows as
 // one digit chunk per sorted position.
 // ---------------------------------------------------------------------------
-template <int GPL, int LPR, int TB>
-__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false>())) gemv_gateup_kernel(QMat G, QMat Up, XDigits xd,
+template <int GPL, int LPR, int TB, bool G32>
+__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false, G32>())) gemv_gateup_kernel(QMat G, QMat Up, XDigits xd,
                                                                  XDigits hd, GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;       // lane groups per block
     constexpr int NR = 64;                     // row tasks per block
@@ -290,13 +296,13 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false>())) g
     // groups), so waves 0-1 read gate and waves 2-3 up.
     static_assert(NSTEP * (64 / LPR) == 16, "16 row tasks per wave");
     const bool up_wave = __builtin_amdgcn_readfirstlane(wave_id()) >= 2;
-    const RowSrc<GPL> src = row_src<GPL, LPR>(up_wave ? Up : G, e, lr);
+    const RowSrc<GPL> src = row_src<GPL, LPR, G32>(up_wave ? Up : G, e, lr);
     auto row_at = [&](int step) { return row0 + ((slot * NSTEP + step) & 31); };
 
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
         XReg<GPL> xr[TB];
-        stream_rows<GPL, LPR, TB, U, NSTEP>(
+        stream_rows<GPL, LPR, TB, U, NSTEP, G32>(
             xr, nt, lr, src, row_at,
             [&]() {
 #pragma unroll
@@ -325,8 +331,8 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false>())) g
 // Routed mode adds w * y into out[token] with f32 atomics (out was cleared by
 // the preparation kernel); direct mode stores y to out[pos].
 // ---------------------------------------------------------------------------
-template <int GPL, int LPR, int TB>
-__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true>())) gemv_down_kernel(QMat D, XDigits hd,
+template <int GPL, int LPR, int TB, bool G32>
+__global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true, G32>())) gemv_down_kernel(QMat D, XDigits hd,
                                                                float *__restrict__ out,
                                                                GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;
@@ -341,7 +347,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true>())) ge
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
     const int row0 = blockIdx.x * NR + slot * NSTEP;
     const bool routed = r.rec != nullptr;
-    const RowSrc<GPL> src = row_src<GPL, LPR>(D, e, lr);
+    const RowSrc<GPL> src = row_src<GPL, LPR, G32>(D, e, lr);
     // rows past O re-read row O-1 and are never emitted
     auto row_at = [&](int step) { return min(row0 + step, O - 1); };
 
@@ -367,7 +373,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true>())) ge
                 }
             }
         };
-        stream_rows<GPL, LPR, TB, U, NSTEP>(xr, nt, lr, src, row_at, prologue,
+        stream_rows<GPL, LPR, TB, U, NSTEP, G32>(xr, nt, lr, src, row_at, prologue,
                                             [&](int step, int j, float v) {
                                                 const int o = row0 + step;
                                                 if (o < O) {
@@ -444,11 +450,16 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
     const GemvShape s = choose_shape(gate.cols / 64);
     const int tb = tokens_per_pass(s, r, true);
     const dim3 grid(gate.rows / 32, r.rec ? r.max_active : 1);
-#define X(G_, L_, T_)                                                                      \
-    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                          \
-        hipLaunchKernelGGL((gemv_gateup_kernel<G_, L_, T_>), grid, dim3(GV_THREADS), 0, st, \
-                           gate, up, xd, hd, r);                                           \
-        return hipGetLastError();                                                          \
+    const bool g32 = gate.group == 32;
+#define X(G_, L_, T_)                                                                          \
+    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                              \
+        if (g32)                                                                               \
+            hipLaunchKernelGGL((gemv_gateup_kernel<G_, L_, T_, true>), grid, dim3(GV_THREADS), \
+                               0, st, gate, up, xd, hd, r);                                    \
+        else                                                                                   \
+            hipLaunchKernelGGL((gemv_gateup_kernel<G_, L_, T_, false>), grid, dim3(GV_THREADS), \
+                               0, st, gate, up, xd, hd, r);                                    \
+        return hipGetLastError();                                                              \
     }
     QMOE_GEMV_SHAPES(X)
 #undef X
@@ -460,11 +471,16 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
     const GemvShape s = choose_shape(down.cols / 64);
     const int tb = tokens_per_pass(s, r, false);
     const dim3 grid((down.rows + 63) / 64, r.rec ? r.max_active : 1);
-#define X(G_, L_, T_)                                                                    \
-    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                        \
-        hipLaunchKernelGGL((gemv_down_kernel<G_, L_, T_>), grid, dim3(GV_THREADS), 0, st, \
-                           down, hd, out, r);                                            \
-        return hipGetLastError();                                                        \
+    const bool g32 = down.group == 32;
+#define X(G_, L_, T_)                                                                        \
+    if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                            \
+        if (g32)                                                                             \
+            hipLaunchKernelGGL((gemv_down_kernel<G_, L_, T_, true>), grid, dim3(GV_THREADS), \
+                               0, st, down, hd, out, r);                                     \
+        else                                                                                 \
+            hipLaunchKernelGGL((gemv_down_kernel<G_, L_, T_, false>), grid, dim3(GV_THREADS), \
+                               0, st, down, hd, out, r);                                     \
+        return hipGetLastError();                                                            \
     }
     QMOE_GEMV_SHAPES(X)
 #undef X

@@ -14,7 +14,22 @@ struct QMat {
     int64_t q_stride;   // bytes between experts
     int64_t s_stride;   // floats between experts
     int rows, cols;     // O, I (cols % 64 == 0)
+    int group;          // inputs per scale: 32, or a multiple of 64
 };
+
+// Scales per row.
+__host__ __device__ inline int scales_per_row(const QMat &m) {
+    return (m.cols + m.group - 1) / m.group;
+}
+
+// For group 64 * 2^j: j, so that 64-input group g has scale g >> j; for a
+// group at least as wide as the row: 31 (every g has scale 0).
+__host__ __device__ inline int group_shift(const QMat &m) {
+    if (m.group >= m.cols) return 31;
+    int j = 0;
+    while ((64 << j) < m.group) j++;
+    return j;
+}
 
 // Worklist outputs inside a workspace.
 struct Worklist {

@@ -1,0 +1,82 @@
+// Prefill down projection on the matrix cores (see mfma.hip for the design).
+#include "mfma_loop.h"
+
+namespace qmoe {
+
+// ---------------------------------------------------------------------------
+// down: block = (256 features of H, one tile of <=256 rows); wave w:
+// features n0 + 64w + 32j + (lane%32), j = 0, 1.
+// Routed: Y[pos] = w * (D h); direct: out[pos] = D h.
+// ---------------------------------------------------------------------------
+template <int BMK, bool G32>
+__global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
+    QMat D, const uint16_t *__restrict__ h16, float *__restrict__ y, MfmaRoute r) {
+    constexpr int MF = mf_of<BMK>();
+    __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
+        s2[BMK * 64], s3[BMK * 64];
+    __shared__ float sW[BMK];
+
+    const int H = D.rows, F = D.cols, ng = F / 64;
+    int tile, cb;
+    if (!work_item<BMK>(r, (H + 255) / 256, tile, cb)) return;
+    TileInfo ti;
+    if (!tile_info<BMK>(r, tile, ti)) return;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int hh = lane >> 5;
+    const bool routed = r.wl.pairs != nullptr;
+    // routing weight of each row, fetched before the main loop (the barriers
+    // inside it publish sW)
+    for (int m = tid; m < BMK; m += MF_THREADS)
+        sW[m] = m >= ti.rows ? 0.f : routed ? r.topk_w[r.wl.pairs[ti.pos0 + m]] : 1.0f;
+
+    LoopSrc<MF> src;
+    src.a = make_rsrc(h16, (int64_t)r.h_rows * F * 2);
+    src.gshift = group_shift(D);
+    tile_offsets(src, ti.rows, F, [&](int m) -> int64_t { return ti.pos0 + m; });
+    int ncol[NF];
+#pragma unroll
+    for (int j = 0; j < NF; j++) {
+        ncol[j] = cb * 256 + 64 * w + 32 * j + (lane & 31);
+        const int nn = ncol[j] < H ? ncol[j] : 0;
+        src.q[j] = make_rsrc(D.q + (int64_t)ti.e * D.q_stride, (int64_t)H * (F / 2));
+        const int spr = scales_per_row(D);
+        src.s[j] = make_rsrc(D.s + (int64_t)ti.e * D.s_stride, (int64_t)H * spr * 4);
+        src.qoff[j] = (uint32_t)(nn * (F / 2) + 16 * hh);
+        src.soff[j] = (uint32_t)(nn * spr * 4 + (G32 ? 4 * hh : 0));
+    }
+
+    Frags<MF> fr;
+    run_mainloop<MF, G32>(fr, src, ng, ti.rows, s0, s1, s2, s3);
+
+#pragma unroll
+    for (int i = 0; i < MF; i++) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            const int m = acc_row(i, v, lane);
+            if (m < ti.rows) {
+                const int pos = ti.pos0 + m;
+                const float wgt = sW[m];
+#pragma unroll
+                for (int j = 0; j < NF; j++)
+                    if (ncol[j] < H) y[(int64_t)pos * H + ncol[j]] = wgt * fr.acc[i][j][v];
+            }
+        }
+    }
+}
+
+// out[t] = sum_j Y[inv[t*k + j]], slots in order; 4 floats per thread.
+hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y, const MfmaRoute &r,
+                            hipStream_t st) {
+    constexpr int BMK = DOWN_BM;
+    const int64_t items = r.wl.pairs ? (int64_t)r.max_tiles * (BM / BMK) : (r.ntok + BMK - 1) / BMK;
+    const dim3 grid(xcd_grid(items * ((down.rows + 255) / 256)));
+    if (down.group == 32)
+        hipLaunchKernelGGL((mfma_down_kernel<BMK, true>), grid, dim3(MF_THREADS), 0, st, down, h16,
+                           y, r);
+    else
+        hipLaunchKernelGGL((mfma_down_kernel<BMK, false>), grid, dim3(MF_THREADS), 0, st, down,
+                           h16, y, r);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -182,18 +182,19 @@ def make_logits(wl: Workload, gen, tokens=None):
     raise ValueError(wl.logits)
 
 
-def layer_weights(gen, experts, hidden, inter, device="cpu"):
-    """Stacked int4 codes and scales for gate/up [E,F,H] and down [E,H,F].
+def layer_weights(gen, experts, hidden, inter, device="cpu", group=GROUP):
+    """Stacked int4 codes and scales for gate/up [E,F,H] and down [E,H,F],
+    one scale per `group` inputs (64 unless asked otherwise).
 
     Draw order q (gate, up, down), then s (gate, up, down)."""
     qg = rand_q(gen, (experts, inter, hidden), device)
     qu = rand_q(gen, (experts, inter, hidden), device)
     qd = rand_q(gen, (experts, hidden, inter), device)
-    sg = rand_scales(gen, (experts, inter, math.ceil(hidden / GROUP)),
+    sg = rand_scales(gen, (experts, inter, math.ceil(hidden / group)),
                      device=device)
-    su = rand_scales(gen, (experts, inter, math.ceil(hidden / GROUP)),
+    su = rand_scales(gen, (experts, inter, math.ceil(hidden / group)),
                      device=device)
-    sd = rand_scales(gen, (experts, hidden, math.ceil(inter / GROUP)),
+    sd = rand_scales(gen, (experts, hidden, math.ceil(inter / group)),
                      device=device)
     return dict(qg=qg, qu=qu, qd=qd, sg=sg, su=su, sd=sd)
 

@@ -41,10 +41,10 @@ def orc():
 class Layer:
     """Codes q (kept for the oracle) and the device layer packed by qmoe_pack."""
 
-    def __init__(self, E, H, F, seed, device="cuda", gen_device="cpu"):
+    def __init__(self, E, H, F, seed, device="cuda", gen_device="cpu", group=64):
         gen = synth.generator(seed, gen_device)
-        w = synth.layer_weights(gen, E, H, F, device=gen_device)
-        self.E, self.H, self.F = E, H, F
+        w = synth.layer_weights(gen, E, H, F, device=gen_device, group=group)
+        self.E, self.H, self.F, self.group = E, H, F, group
         self.q = {k: w[k] for k in ("qg", "qu", "qd")}
         self.s = {k: w[k] for k in ("sg", "su", "sd")}
         dq = {k: v.to(device) for k, v in self.q.items()}
@@ -52,7 +52,8 @@ class Layer:
         self.s_dev = {k: v.to(device).contiguous() for k, v in self.s.items()}
         del dq
         self.dev = qm.QLayer(self.packed["qg"], self.s_dev["sg"], self.packed["qu"],
-                             self.s_dev["su"], self.packed["qd"], self.s_dev["sd"], H, F)
+                             self.s_dev["su"], self.packed["qd"], self.s_dev["sd"], H, F,
+                             group=group)
         self.gen = gen
 
     def oracle_subset(self, experts):
@@ -87,7 +88,7 @@ class Layer:
             return np.zeros((x.shape[0], self.H))
         stacks = self.oracle_subset(used)
         out, _ = orc().layer(*stacks, self.H, self.F, x, ids2.numpy().astype(np.int32),
-                             w.numpy())
+                             w.numpy(), gs=self.group)
         return out
 
 

@@ -88,7 +88,14 @@ def test_layer_rejections(lib):
     d2 = layer_desc()
     d2.gate.struct_size = 4
     assert call_layer(lib, d2) == 7
-    assert call_layer(lib, layer_desc(group=128)) == 4                  # UNSUPPORTED
+    assert call_layer(lib, layer_desc(group=96)) == 4                   # UNSUPPORTED
+    assert call_layer(lib, layer_desc(group=48)) == 4
+    d3 = layer_desc(group=128)
+    d3.down.group = 64                                                  # groups differ
+    assert call_layer(lib, d3) == 2
+    d4 = layer_desc(group=32)
+    d4.gate.s_expert_stride = 128 * 256 // 64                           # too few scales for 32
+    assert call_layer(lib, d4) == 2
     assert call_layer(lib, layer_desc(H=200)) == 4
     assert call_layer(lib, layer_desc(E=0)) == 2                        # SHAPE
     assert call_layer(lib, layer_desc(E=2000)) == 2

@@ -1,0 +1,83 @@
+"""Group sizes other than 64 on the GPU: 32, 128 and one scale per row (a
+group as wide as the row, the per-row int4 format), against the oracle run
+with the same group size (the oracle takes any group; its pins cover the
+scale index for groups 2, 4 and wider than the row)."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_int4_expert_amd as qm
+import synth
+from gpu_util import BF16_TOL, F32_TOL, Layer, orc, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GROUPS = [32, 128, "row"]
+
+
+def _gs(group, cols):
+    return cols if group == "row" else group
+
+
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("rows,cols", [(64, 256), (256, 4096), (130, 1536)])
+def test_matvec_one_hot_bit_exact(group, rows, cols):
+    # x = e_j: y[o] = s[o, j // gs] * q[o, j] exactly, for every kernel shape
+    gs = _gs(group, cols)
+    say(f"one-hot matvec {rows}x{cols} group {gs}")
+    g = synth.generator(60)
+    q = synth.rand_q(g, (rows, cols))
+    s = synth.rand_scales(g, (rows, -(-cols // gs)))
+    pk = qm.qmoe_pack(q.to(DEV))
+    for j in (0, 31, 32, 63, 64, cols - 1):
+        x = torch.zeros(1, cols)
+        x[0, j] = 1.0
+        y = qm.qmoe_matvec(pk, s.to(DEV), cols, x.to(DEV), group=gs).cpu()
+        ref = (q[:, j].to(torch.float64) * s[:, j // gs].to(torch.float64)).to(torch.float32)
+        assert torch.equal(y[0], ref), (j, float((y[0] - ref).abs().max()))
+
+
+@pytest.mark.parametrize("group", GROUPS)
+def test_matvec_random(group):
+    rows, cols = 256, 2048
+    gs = _gs(group, cols)
+    say(f"matvec {rows}x{cols} group {gs}")
+    g = synth.generator(61)
+    q = synth.rand_q(g, (rows, cols))
+    s = synth.rand_scales(g, (rows, -(-cols // gs)))
+    x = synth.rand_x(g, (3, cols))
+    y = qm.qmoe_matvec(qm.qmoe_pack(q.to(DEV)), s.to(DEV), cols, x.to(DEV), group=gs).cpu()
+    pq, _ = orc().pack(q.numpy())
+    ref = orc().matvec(pq, s.numpy(), cols, x.numpy(), gs=gs)
+    assert rel_l2(y.numpy(), ref) <= F32_TOL
+
+
+@pytest.mark.parametrize("group", GROUPS)
+@pytest.mark.parametrize("dtype,T,k", [("f32", 23, 4), ("bf16", 23, 4), ("bf16", 700, 2)])
+def test_layer_groups(group, dtype, T, k):
+    E, H, F = 4 if T > 100 else 16, 512, 256
+    gs = _gs(group, max(H, F))
+    say(f"layer E={E} H={H} F={F} T={T} k={k} {dtype} group {gs}")
+    L = Layer(E, H, F, seed=62, group=gs)
+    wl = synth.Workload("g", E, H, F, k, T, dtype, "normal", 63)
+    x, ids, w = synth.layer_inputs(wl, synth.generator(64))
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref = L.oracle_layer(x, ids, w)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("group", [32, 128])
+def test_decode_layer_full_size_groups(group):
+    # the 128-expert decode layer at 16 tokens, sampled tokens against the oracle
+    say(f"decode layer E=128 H=4096 F=1536 T=16 group {group}")
+    L = Layer(128, 4096, 1536, seed=65, gen_device="cuda", group=group)
+    wl = synth.LAYERS["decode_e128_t16"]
+    x, ids, w = synth.layer_inputs(wl, synth.generator(66))
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    toks = [0, 7, 15]
+    ref = L.oracle_layer(x, ids, w, tokens=toks)
+    err = rel_l2(out[toks], ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= F32_TOL
