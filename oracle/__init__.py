@@ -11,9 +11,9 @@ floating input is widened exactly to float64 before the call (f32 and bf16
 are exact in double), so the oracle sees the same numbers the GPU sees.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_*``):
-pack/unpack, matvec, pair, silu, ffn, worklist, layer and route are all
-pinned by hand-written values, closed forms or brute force; none is "parity
-unpinned".
+pack/unpack, import_twos, detect_group, matvec, pair, silu, ffn, worklist,
+layer and route are all pinned by hand-written values, closed forms or brute
+force; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -81,6 +81,10 @@ def load(path=None):
                               i64, vp, vp, i64, vp]
     lib.orc_route.restype = None
     lib.orc_route.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.orc_import_twos.restype = None
+    lib.orc_import_twos.argtypes = [vp, i64, i64, vp]
+    lib.orc_detect_group.restype = i64
+    lib.orc_detect_group.argtypes = [i64, i64, i64]
     if path is None:
         _lib = lib
     return lib
@@ -222,3 +226,14 @@ class Oracle:
         w = np.empty((tokens, k), np.float32)
         self.lib.orc_route(_p(logits), tokens, experts, k, _p(ids), _p(w))
         return ids, w
+
+    def import_twos(self, twos, cols):
+        """Two's-complement nibble container -> offset container."""
+        twos = _c(_np(twos), np.uint8)
+        rows = int(np.prod(twos.shape[:-1]))
+        out = np.empty_like(twos)
+        self.lib.orc_import_twos(_p(twos), rows, cols, _p(out))
+        return out
+
+    def detect_group(self, rows, cols, scale_bytes):
+        return int(self.lib.orc_detect_group(rows, cols, scale_bytes))

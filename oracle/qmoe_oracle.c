@@ -31,7 +31,11 @@
  *    layer.
  *  - the same pull request, the quoted issue's list of CPU work: the
  *    router's top-K picks with one "taken" flag per expert, K passes over
- *    the E logits.
+ *    the E logits; and detect_group_size(), which recovers gs from the
+ *    scale array's byte count over the candidates 16..256.
+ *  - comment "implementation complete but system-instability": the GPU
+ *    container holds two's-complement nibbles, reached from the offset
+ *    container by a byte XOR of 0x88 (the import below goes the other way).
  *
  * Readings taken where the pages are silent (each listed with its reason in
  * the design notes of this repository):
@@ -257,4 +261,23 @@ void orc_route(const float *logits, int64_t tokens, int64_t experts, int64_t k,
     }
     free(ex);
     free(taken);
+}
+
+/* ---- container import and group-size detection ---------------------------
+ * Two's-complement nibble container -> offset container: each nibble n
+ * (value n - 16 if n >= 8, else n) becomes value + 8, i.e. n XOR 8; both
+ * nibbles of a byte at once is XOR 0x88. */
+void orc_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *packed) {
+    int64_t n = orc_packed_bytes(rows, cols);
+    for (int64_t b = 0; b < n; b++) packed[b] = (uint8_t)(twos[b] ^ 0x88);
+}
+
+/* The group size whose scale array (rows * ceil(cols / gs) f32) has exactly
+ * scale_bytes bytes, trying 16, 32, 48, 64, 96, 128, 192, 256 in that order;
+ * 0 when none fits. */
+int64_t orc_detect_group(int64_t rows, int64_t cols, int64_t scale_bytes) {
+    static const int64_t cand[8] = {16, 32, 48, 64, 96, 128, 192, 256};
+    for (int c = 0; c < 8; c++)
+        if (orc_scale_count(rows, cols, cand[c]) * 4 == scale_bytes) return cand[c];
+    return 0;
 }

@@ -495,4 +495,49 @@ def pin_route_weights_sum_to_one(orc):
     assert np.all(np.diff(w, axis=1) <= 0), "slot order is descending logit"
 
 
+# ------------------------------------------------ import / group detection ---
+
+def pin_import_twos_exhaustive(orc):
+    """Every byte of a two's-complement container: after import, each nibble
+    decodes (offset - 8) to the signed value the two's-complement nibble
+    held (n - 16 for n >= 8)."""
+    twos = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    packed = orc.import_twos(twos, 512)
+    q = orc.unpack(packed, 512)[0]
+    for b in range(256):
+        lo, hi = b & 15, b >> 4
+        assert q[2 * b] == (lo - 16 if lo >= 8 else lo), b
+        assert q[2 * b + 1] == (hi - 16 if hi >= 8 else hi), b
+
+
+def pin_import_twos_pad_nibble(orc):
+    """Odd I: a two's-complement zero pad nibble imports as the offset pad 8."""
+    twos = np.array([[0x07]], dtype=np.uint8)    # element 0 = 7, pad nibble 0
+    packed = orc.import_twos(twos, 1)
+    assert packed.tolist() == [[0x8F]]
+
+
+def pin_detect_group_pages(orc):
+    """kv_b header: 28,672 rows of 512 inputs with 917,504 scale bytes is gs
+    64; the 6144 x 2048 expert matrices (786,432 B of g64 scales) likewise;
+    one scale per row (4 B a row) of 512 inputs matches no candidate (the
+    widest, 256, still needs two scales per row)."""
+    assert orc.detect_group(28672, 512, 917504) == 64
+    assert orc.detect_group(2048, 6144, 786432) == 64
+    assert orc.detect_group(6144, 2048, 786432) == 64
+    assert orc.detect_group(28672, 512, 28672 * 4) == 0
+
+
+def pin_detect_group_brute(orc):
+    """For every candidate and a few shapes, the detected size reproduces the
+    byte count, and no smaller candidate does."""
+    cands = [16, 32, 48, 64, 96, 128, 192, 256]
+    for rows, cols in [(7, 512), (3, 4096), (5, 100), (2, 1536)]:
+        for gs in cands:
+            nbytes = rows * (-(-cols // gs)) * 4
+            got = orc.detect_group(rows, cols, nbytes)
+            assert got != 0 and rows * (-(-cols // got)) * 4 == nbytes
+            assert all(rows * (-(-cols // c)) * 4 != nbytes for c in cands if c < got)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -47,6 +47,9 @@ MUTANTS = [
      "double key = (double)l[e];"),
     ("route_weights_not_normalised", "w[t * k + s] = (float)(ex[s] / sum);",
      "w[t * k + s] = (float)ex[s];"),
+    ("import_xor_low_nibble_only", "packed[b] = (uint8_t)(twos[b] ^ 0x88);",
+     "packed[b] = (uint8_t)(twos[b] ^ 0x08);"),
+    ("detect_group_largest_first", "for (int c = 0; c < 8; c++)", "for (int c = 7; c >= 0; c--)"),
 ]
 
 
