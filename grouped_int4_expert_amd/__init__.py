@@ -58,7 +58,8 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_pack", "qmoe_unpack", "qmoe_matvec_workspace_bytes", "qmoe_matvec",
            "qmoe_expert_ffn_workspace_bytes", "qmoe_expert_ffn",
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
-           "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route"]
+           "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route",
+           "qmoe_import_twos", "qmoe_detect_group"]
 
 _lib = None
 
@@ -97,6 +98,8 @@ def load(path: str | None = None):
         "qmoe_layer_ws_layout": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32,
                                                 ctypes.POINTER(qmoe_layer_ws_view)]),
         "qmoe_route": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
+        "qmoe_import_twos": (ctypes.c_int, [vp, i64, i64, vp, vp]),
+        "qmoe_detect_group": (i32, [i64, i64, i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -307,6 +310,22 @@ def qmoe_worklist(topk_ids, experts, ws=None, stream=None):
     out["pairs"] = out["pairs"][:n]
     out["inv"] = out["inv"][:n]
     return out
+
+
+def qmoe_import_twos(twos, cols, out=None, stream=None):
+    """Two's-complement nibble container (uint8 [rows, ceil(cols/2)]) ->
+    offset container (what qmoe_pack writes); out may be twos itself."""
+    _dev(twos, "twos", torch.uint8)
+    rows = twos.shape[0]
+    out = out if out is not None else torch.empty_like(twos)
+    _check(load().qmoe_import_twos(_ptr(twos), rows, cols, _ptr(out), _stream(stream)),
+           "qmoe_import_twos")
+    return out
+
+
+def qmoe_detect_group(rows: int, cols: int, scale_bytes: int) -> int:
+    """Group size from a scale array's byte count (0: no candidate fits)."""
+    return int(load().qmoe_detect_group(rows, cols, scale_bytes))
 
 
 def qmoe_route(logits, k, ids=None, w=None, stream=None):

@@ -340,6 +340,24 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     return status_of(e);
 }
 
+int qmoe_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *packed,
+                     void *stream) {
+    if (rows < 0 || cols < 0) return QMOE_ERR_SHAPE;
+    const int64_t n = packed_bytes(rows, cols);
+    if (n == 0) return QMOE_OK;
+    if (!twos || !packed) return QMOE_ERR_NULL;
+    if (twos != packed && overlap(twos, n, packed, n)) return QMOE_ERR_ALIAS;
+    return status_of(launch_import_twos(twos, rows, cols, packed, as_stream(stream)));
+}
+
+int32_t qmoe_detect_group(int64_t rows, int64_t cols, int64_t scale_bytes) {
+    static const int64_t cand[8] = {16, 32, 48, 64, 96, 128, 192, 256};
+    if (rows <= 0 || cols <= 0 || scale_bytes <= 0) return 0;
+    for (int64_t gs : cand)
+        if (scale_count(rows, cols, gs) * 4 == scale_bytes) return (int32_t)gs;
+    return 0;
+}
+
 int qmoe_route(const float *logits, int32_t tokens, int32_t experts, int32_t k,
                int32_t *topk_ids, float *topk_w, void *stream) {
     if (tokens < 0 || experts < 1 || k < 1 || k > experts) return QMOE_ERR_SHAPE;

@@ -53,6 +53,8 @@ struct XDigits {
 
 hipError_t launch_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
                        int32_t *n_bad, hipStream_t st);
+hipError_t launch_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *packed,
+                              hipStream_t st);
 hipError_t launch_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
                          hipStream_t st);
 

@@ -50,6 +50,25 @@ __global__ void unpack_kernel(const uint8_t *__restrict__ packed, int64_t rows, 
     }
 }
 
+// Two's-complement nibble container (what the pages' GPU upload holds) to
+// the offset container: a nibble n becomes n XOR 8 (signed value + 8), so a
+// byte XOR 0x88.  16 bytes per thread where both buffers are 16-byte aligned,
+// single bytes otherwise; in place is allowed.
+__global__ void import_twos_kernel(const uint8_t *twos, int64_t n, uint8_t *packed, int vec) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t done = 0;
+    if (vec) {
+        const int64_t n16 = n / 16;
+        for (int64_t j = i; j < n16; j += stride) {
+            const u32x4 v = ((const u32x4 *)twos)[j];
+            ((u32x4 *)packed)[j] = v ^ 0x88888888u;
+        }
+        done = n16 * 16;
+    }
+    for (int64_t j = done + i; j < n; j += stride) packed[j] = (uint8_t)(twos[j] ^ 0x88u);
+}
+
 __global__ void zero_i32_kernel(int32_t *p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -80,4 +99,14 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8
     return hipGetLastError();
 }
 
+
+hipError_t launch_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *packed,
+                              hipStream_t st) {
+    const int64_t n = rows * ((cols + 1) / 2);
+    const int vec = ((reinterpret_cast<uintptr_t>(twos) | reinterpret_cast<uintptr_t>(packed)) &
+                     15u) == 0;
+    hipLaunchKernelGGL(import_twos_kernel, dim3(grid_for(vec ? n / 16 + 1 : n, 256)), dim3(256),
+                       0, st, twos, n, packed, vec);
+    return hipGetLastError();
+}
 }  // namespace qmoe

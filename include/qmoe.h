@@ -174,6 +174,24 @@ int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k,
                   int32_t *pairs, int32_t *inv, int32_t *n_invalid, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* Import of the two's-complement nibble container (the layout the pages'
+ * GPU upload produces; colibri pull request "cuda+engine: full fmt=4
+ * (grouped int4 gs=64) support", comment "implementation complete but
+ * system-instability": offset nibbles become two's complement by a byte XOR
+ * of 0x88) back into the offset container this library reads: every byte
+ * XOR 0x88.  twos and packed are device buffers of rows * ceil(cols/2)
+ * bytes; packed == twos (in place) is allowed, any other overlap is
+ * QMOE_ERR_ALIAS.  Bit-exact. */
+int qmoe_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *packed,
+                     void *stream);
+
+/* Group size of a matrix from its scale array's byte count, as the pages'
+ * loader does (same pull request, quoted issue's list of CPU work,
+ * detect_group_size()): the first of 16, 32, 48, 64, 96, 128, 192, 256 with
+ * rows * ceil(cols / gs) * 4 == scale_bytes, or 0 when none fits.  Host
+ * only; launches nothing. */
+int32_t qmoe_detect_group(int64_t rows, int64_t cols, int64_t scale_bytes);
+
 /* Router, the step ahead of the layer: for each token, the k experts with
  * the largest logits and their routing weights (colibri pull request
  * "cuda+engine: full fmt=4 (grouped int4 gs=64) support", the quoted issue's

@@ -180,3 +180,23 @@ def test_route_rejections(lib):
     assert lib.qmoe_route(L, 4, 128, 8, L + 64, W, None) == 6     # ids inside the logits
     assert lib.qmoe_route(L, 4, 128, 8, I, I + 16, None) == 6     # ids and weights overlap
     assert lib.qmoe_route(L, 0, 128, 8, None, None, None) == 0    # nothing to do
+
+
+def test_import_twos_rejections(lib):
+    assert lib.qmoe_import_twos(None, 4, 64, FAKE, None) == 1
+    assert lib.qmoe_import_twos(FAKE, -1, 64, FAKE, None) == 2
+    assert lib.qmoe_import_twos(FAKE, 4, 64, FAKE + 16, None) == 6   # partial overlap
+    assert lib.qmoe_import_twos(FAKE, 0, 64, FAKE, None) == 0        # nothing to do
+
+
+def test_detect_group_matches_oracle(lib):
+    # host-only entry point: the library and the oracle agree everywhere
+    import oracle
+    orc = oracle.Oracle()
+    for rows in (1, 3, 7, 2048):
+        for cols in (1, 31, 64, 100, 512, 1536, 4096, 6144):
+            for gs in (8, 16, 32, 48, 64, 96, 128, 192, 256, 512, 100000):
+                nb = rows * (-(-cols // gs)) * 4
+                for b in (nb, nb + 4, nb - 4):
+                    assert lib.qmoe_detect_group(rows, cols, b) == orc.detect_group(rows, cols, b)
+    assert lib.qmoe_detect_group(28672, 512, 917504) == 64

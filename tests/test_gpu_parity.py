@@ -339,3 +339,18 @@ def test_layer_graph_replays_match_eager(dtype):
         torch.cuda.synchronize()
         assert torch.isfinite(out).all()
         assert rel_l2(out.cpu().numpy(), eager.cpu().numpy()) <= 1e-6, rep
+
+
+@pytest.mark.parametrize("rows,cols,offset", [(5, 4096, 0), (7, 33, 0), (3, 1000, 3), (1, 1, 0)])
+def test_import_twos(rows, cols, offset):
+    say(f"import two's complement rows={rows} cols={cols} offset={offset}")
+    g = synth.generator(70)
+    rb = (cols + 1) // 2
+    raw = torch.randint(0, 256, (rows * rb + offset,), generator=g, dtype=torch.int64).to(torch.uint8)
+    twos = raw[offset:].reshape(rows, rb)
+    ref = orc().import_twos(twos.numpy(), cols)
+    d = raw.to(DEV)[offset:].view(rows, rb)
+    got = qm.qmoe_import_twos(d, cols).cpu().numpy()
+    assert np.array_equal(got, ref)
+    qm.qmoe_import_twos(d, cols, out=d)                  # in place
+    assert np.array_equal(d.cpu().numpy(), ref)
