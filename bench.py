@@ -77,14 +77,23 @@ def make_layer(qm, synth, seed, dev):
     return layer, codes, {k: w[k] for k in ("sg", "su", "sd")}
 
 
-def load_traffic(kernel_src):
-    """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel source (null otherwise)."""
+def source_hash(paths):
+    """sha256[:16] of the concatenated kernel sources."""
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_srcs):
+    """HBM traffic per launch from the committed counter summary, if it was
+    taken on the current kernel sources (null otherwise)."""
     path = os.path.join(ROOT, "profiles", "mfma_gateup_prefill_e128_t8192_counters.md")
     if not os.path.exists(path):
         return None
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    h = source_hash(kernel_srcs)
     text = open(path).read()
     if f"source sha256[:16]: {h}" not in text:
         return None
@@ -345,7 +354,8 @@ def main():
     value = 100.0 * roof_step / (ms_step * 1e-3)
     dec_roof = roof_step - p_roof
     achieved = p_gu_flops / (gateup_ms * 1e-3)
-    kernel_src = os.path.join(ROOT, "grouped_int4_expert_amd", "csrc", "mfma.hip")
+    kernel_src = [os.path.join(ROOT, "grouped_int4_expert_amd", "csrc", f)
+                  for f in ("mfma.hip", "mfma_loop.h")]
     rec = {
         "metric": "int4-g64 MoE expert GB/s (decode) + TFLOP/s (8K prefill), % of roofline",
         "value": round(value, 3),
