@@ -59,7 +59,8 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_expert_ffn_workspace_bytes", "qmoe_expert_ffn",
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
            "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route",
-           "qmoe_import_twos", "qmoe_detect_group"]
+           "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
+           "qmoe_cache_prepare", "qmoe_cache_resident"]
 
 _lib = None
 
@@ -100,6 +101,12 @@ def load(path: str | None = None):
         "qmoe_route": (ctypes.c_int, [vp, i32, i32, i32, vp, vp, vp]),
         "qmoe_import_twos": (ctypes.c_int, [vp, i64, i64, vp, vp]),
         "qmoe_detect_group": (i32, [i64, i64, i64]),
+        "qmoe_cache_create": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc),
+                                             ctypes.POINTER(qmoe_layer_desc),
+                                             ctypes.POINTER(ctypes.c_void_p)]),
+        "qmoe_cache_destroy": (None, [vp]),
+        "qmoe_cache_prepare": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.POINTER(i64), vp]),
+        "qmoe_cache_resident": (i32, [vp, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -236,6 +243,66 @@ class QLayer:
         _check(load().qmoe_layer_ws_layout(ctypes.byref(self.desc), tokens, k, x_dtype,
                                            ctypes.byref(v)), "qmoe_layer_ws_layout")
         return v
+
+
+class HostLayer:
+    """Stacked weights of one MoE layer in host memory (pinned CPU tensors:
+    gate/up packed [E, F, H/2] + scales, down packed [E, H, F/2] + scales),
+    the backing store of an ExpertCache."""
+
+    def __init__(self, pg, sg, pu, su, pd, sd, hidden, inter, group=64):
+        self.tensors = [pg, sg, pu, su, pd, sd]
+        for t, n in zip(self.tensors, ("pg", "sg", "pu", "su", "pd", "sd")):
+            if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_contiguous():
+                raise TypeError(f"{n} must be a contiguous CPU tensor (pinned for async copies)")
+        self.experts = pg.shape[0]
+        self.hidden, self.inter, self.group = hidden, inter, group
+        d = qmoe_layer_desc()
+        d.struct_size = ctypes.sizeof(qmoe_layer_desc)
+        d.experts, d.hidden, d.inter, d.group = self.experts, hidden, inter, group
+        d.gate = make_qmat(pg, sg, hidden, group)
+        d.up = make_qmat(pu, su, hidden, group)
+        d.down = make_qmat(pd, sd, inter, group)
+        self.desc = d
+
+
+class ExpertCache:
+    """S expert slots in HBM (a device QLayer with S experts) in front of a
+    HostLayer; prepare() copies the routed experts that are missing."""
+
+    def __init__(self, host: HostLayer, slots: QLayer):
+        self.host, self.slots = host, slots
+        h = ctypes.c_void_p()
+        _check(load().qmoe_cache_create(ctypes.byref(host.desc), ctypes.byref(slots.desc),
+                                        ctypes.byref(h)), "qmoe_cache_create")
+        self.handle = h
+        self._lib = load()
+
+    def prepare(self, host_ids, slot_ids=None, stream=None):
+        """host_ids int32 CPU [T, k] -> (slot_ids int32 CPU [T, k], bytes copied)."""
+        if host_ids.is_cuda or host_ids.dtype != torch.int32 or not host_ids.is_contiguous():
+            raise TypeError("host_ids must be a contiguous int32 CPU tensor")
+        T, k = host_ids.shape
+        out = slot_ids if slot_ids is not None else torch.empty(T, k, dtype=torch.int32)
+        nb = ctypes.c_int64(0)
+        _check(self._lib.qmoe_cache_prepare(self.handle, _ptr(host_ids), T, k, _ptr(out),
+                                            ctypes.byref(nb), _stream(stream)),
+               "qmoe_cache_prepare")
+        return out, nb.value
+
+    def resident(self, expert):
+        return int(self._lib.qmoe_cache_resident(self.handle, expert))
+
+    def close(self):
+        if self.handle:
+            self._lib.qmoe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover
+            pass
 
 
 def _dtype_code(x):

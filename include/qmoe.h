@@ -192,6 +192,39 @@ int qmoe_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *p
  * only; launches nothing. */
 int32_t qmoe_detect_group(int64_t rows, int64_t cols, int64_t scale_bytes);
 
+/* Expert cache: a layer whose E experts live in host memory, with a fixed
+ * set of S expert slots in HBM in front of it (the VRAM tier of hot experts
+ * of the colibri pull request "cuda+engine: full fmt=4 (grouped int4 gs=64)
+ * support", comments on where decode wall-clock goes and on the
+ * CUDA_EXPERT_GB placement curve).
+ *
+ * qmoe_cache_create: `host` describes the E experts (codes and scales in
+ * host memory; pinned memory lets the copies run asynchronously), `dev` the
+ * S slots (an ordinary device layer descriptor with experts = S, the same
+ * shape and group; its memory stays the caller's).  Returns a host object in
+ * *out (free it with qmoe_cache_destroy); no device work.
+ *
+ * qmoe_cache_prepare: for the routing ids of one call (host int32
+ * [tokens][k]), keep the experts already resident, and for each missing
+ * valid id pick a free slot, else the least recently used slot that neither
+ * this call nor the previous prepare uses, and enqueue its six host->device
+ * copies on `stream`.  Writes slot_ids (host int32 [tokens][k]): the slot of
+ * each pair, -1 for ids outside [0, E).  The caller uploads slot_ids and runs
+ * qmoe_layer on the slot layer `dev` with them, on `stream` or on a stream
+ * that waits for it.  Because the previous call's slots are never evicted,
+ * the copies for call i+1 may overlap the kernels of call i; the copies for
+ * call i+2 must wait for call i's kernels.  *bytes_copied (nullable) = bytes
+ * enqueued.  QMOE_ERR_SHAPE when this call's experts plus the previous call's
+ * other slots exceed S.  Not thread-safe per cache object. */
+typedef struct qmoe_expert_cache qmoe_expert_cache;
+int qmoe_cache_create(const qmoe_layer_desc *host, const qmoe_layer_desc *dev,
+                      qmoe_expert_cache **out);
+void qmoe_cache_destroy(qmoe_expert_cache *cache);
+int qmoe_cache_prepare(qmoe_expert_cache *cache, const int32_t *host_ids, int32_t tokens,
+                       int32_t k, int32_t *slot_ids, int64_t *bytes_copied, void *stream);
+/* Slot holding `expert`, or -1 (not resident or out of range). */
+int32_t qmoe_cache_resident(const qmoe_expert_cache *cache, int32_t expert);
+
 /* Router, the step ahead of the layer: for each token, the k experts with
  * the largest logits and their routing weights (colibri pull request
  * "cuda+engine: full fmt=4 (grouped int4 gs=64) support", the quoted issue's

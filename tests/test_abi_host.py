@@ -200,3 +200,27 @@ def test_detect_group_matches_oracle(lib):
                 for b in (nb, nb + 4, nb - 4):
                     assert lib.qmoe_detect_group(rows, cols, b) == orc.detect_group(rows, cols, b)
     assert lib.qmoe_detect_group(28672, 512, 917504) == 64
+
+
+def test_cache_create_validation(lib):
+    host, dev = layer_desc(E=16), layer_desc(E=4)
+    h = ctypes.c_void_p()
+    assert lib.qmoe_cache_create(ctypes.byref(host), ctypes.byref(dev), ctypes.byref(h)) == 0
+    assert h.value
+    assert lib.qmoe_cache_resident(h, 3) == -1          # nothing resident yet
+    assert lib.qmoe_cache_resident(h, 99) == -1
+    # prepare with no pairs enqueues nothing
+    n = ctypes.c_int64(7)
+    assert lib.qmoe_cache_prepare(h, None, 0, 2, None, ctypes.byref(n), None) == 0
+    assert n.value == 0
+    assert lib.qmoe_cache_prepare(h, None, 2, 2, None, None, None) == 1
+    assert lib.qmoe_cache_prepare(h, FAKE, 2, 0, FAKE, None, None) == 2
+    lib.qmoe_cache_destroy(h)
+    bad = layer_desc(E=4, H=512)                         # other shape
+    assert lib.qmoe_cache_create(ctypes.byref(host), ctypes.byref(bad), ctypes.byref(h)) == 2
+    bad = layer_desc(E=4, size=8)
+    assert lib.qmoe_cache_create(ctypes.byref(host), ctypes.byref(bad), ctypes.byref(h)) == 7
+    nul = layer_desc(E=16)
+    nul.up.q = None
+    assert lib.qmoe_cache_create(ctypes.byref(nul), ctypes.byref(dev), ctypes.byref(h)) == 1
+    assert lib.qmoe_cache_create(None, ctypes.byref(dev), ctypes.byref(h)) == 1
