@@ -60,7 +60,8 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
            "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route",
            "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
-           "qmoe_cache_prepare", "qmoe_cache_resident"]
+           "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_layer_logits_workspace_bytes",
+           "qmoe_layer_logits"]
 
 _lib = None
 
@@ -107,6 +108,9 @@ def load(path: str | None = None):
         "qmoe_cache_destroy": (None, [vp]),
         "qmoe_cache_prepare": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.POINTER(i64), vp]),
         "qmoe_cache_resident": (i32, [vp, i32]),
+        "qmoe_layer_logits_workspace_bytes": (sz, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32]),
+        "qmoe_layer_logits": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, i32,
+                                             vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -422,6 +426,23 @@ def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=Non
     _check(load().qmoe_layer(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
                              _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
            "qmoe_layer")
+    return o
+
+
+def qmoe_layer_logits(layer: QLayer, x, logits, k, out=None, ws=None, stream=None):
+    """Router + layer in one call: route f32 logits [T, E] on the device, then
+    out[t] = sum_j w[t,j] * ffn_{ids[t,j]}(x_t)."""
+    _dev(x, "x")
+    _dev(logits, "logits", torch.float32)
+    code = _dtype_code(x)
+    T = x.shape[0]
+    o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
+                                                device=x.device)
+    nb = int(load().qmoe_layer_logits_workspace_bytes(ctypes.byref(layer.desc), T, k, code))
+    ws = _workspace(nb, x.device, ws)
+    _check(load().qmoe_layer_logits(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(logits), k,
+                                    _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
+           "qmoe_layer_logits")
     return o
 
 

@@ -439,10 +439,12 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int3
                          stream, nullptr, 0);
 }
 
-int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int32_t tokens,
-                  const int32_t *topk_ids, const float *topk_w, int32_t k, float *out,
-                  void *ws, size_t ws_bytes, void *stream, void *const *phase_events,
-                  int32_t n_events) {
+// Everything qmoe_layer_ex checks before launching (the routing arrays are
+// only addressed, never read).
+static int layer_validate(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+                          int32_t tokens, const int32_t *topk_ids, const float *topk_w, int32_t k,
+                          float *out, void *ws, size_t ws_bytes, void *const *phase_events,
+                          int32_t n_events) {
     int s = check_layer_desc(desc);
     if (s) return s;
     if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
@@ -478,7 +480,18 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         overlap(ws, need.bytes, x, xb) || overlap(ws, need.bytes, topk_ids, 4 * n) ||
         overlap(ws, need.bytes, topk_w, 4 * n))
         return QMOE_ERR_ALIAS;
+    return QMOE_OK;
+}
 
+int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, int32_t tokens,
+                  const int32_t *topk_ids, const float *topk_w, int32_t k, float *out,
+                  void *ws, size_t ws_bytes, void *stream, void *const *phase_events,
+                  int32_t n_events) {
+    const int s = layer_validate(desc, x_dtype, x, tokens, topk_ids, topk_w, k, out, ws, ws_bytes,
+                                 phase_events, n_events);
+    if (s || tokens == 0) return s;
+    const int E = desc->experts, H = desc->hidden, F = desc->inter;
+    const int64_t n = (int64_t)tokens * k;
     const LayerWs L = carve_layer(ws, E, H, F, tokens, k, x_dtype);
     const hipStream_t st = as_stream(stream);
     const QMat G = to_qmat(&desc->gate), U = to_qmat(&desc->up), D = to_qmat(&desc->down);
@@ -526,6 +539,43 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         if (e == hipSuccess) e = mark();
     }
     return status_of(e);
+}
+
+size_t qmoe_layer_logits_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
+                                         int32_t k, int32_t x_dtype) {
+    const size_t layer = qmoe_layer_workspace_bytes(desc, tokens, k, x_dtype);
+    if (layer == 0 && tokens > 0) return 0;
+    return layer + 2 * (size_t)align256(4 * (int64_t)tokens * k);
+}
+
+int qmoe_layer_logits(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+                      int32_t tokens, const float *logits, int32_t k, float *out, void *ws,
+                      size_t ws_bytes, void *stream) {
+    int s = check_layer_desc(desc);
+    if (s) return s;
+    if (tokens < 0 || k < 1) return QMOE_ERR_SHAPE;
+    if (!route_supported(desc->experts, k)) return QMOE_ERR_UNSUPPORTED;
+    if (tokens == 0) return QMOE_OK;
+    if (!logits || !ws) return QMOE_ERR_NULL;
+    if (!aligned4(logits)) return QMOE_ERR_ALIGN;
+    const size_t need = qmoe_layer_logits_workspace_bytes(desc, tokens, k, x_dtype);
+    if (need == 0) return QMOE_ERR_UNSUPPORTED;
+    if (ws_bytes < need) return QMOE_ERR_WORKSPACE;
+    const int64_t nl = 4 * (int64_t)tokens * desc->experts;
+    if (overlap(logits, nl, ws, (int64_t)need) || overlap(logits, nl, out, 4 * (int64_t)tokens *
+                                                                          desc->hidden))
+        return QMOE_ERR_ALIAS;
+    // routing arrays at the end of the workspace; the layer's own workspace
+    // (and its worklist view) starts at offset 0
+    const size_t layer = qmoe_layer_workspace_bytes(desc, tokens, k, x_dtype);
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int32_t *ids = reinterpret_cast<int32_t *>(base + layer);
+    float *w = reinterpret_cast<float *>(base + layer + align256(4 * (int64_t)tokens * k));
+    if ((s = layer_validate(desc, x_dtype, x, tokens, ids, w, k, out, ws, layer, nullptr, 0)))
+        return s;
+    const hipError_t e = launch_route(logits, tokens, desc->experts, k, ids, w, as_stream(stream));
+    if (e != hipSuccess) return QMOE_ERR_HIP;
+    return qmoe_layer(desc, x_dtype, x, tokens, ids, w, k, out, ws, layer, stream);
 }
 
 }  // extern "C"

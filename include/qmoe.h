@@ -261,6 +261,19 @@ int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
                int32_t tokens, const int32_t *topk_ids, const float *topk_w,
                int32_t k, float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* The router and the layer in one call, with no host round trip: route f32
+ * logits [tokens][E] with qmoe_route (top-k, softmax over the picked logits)
+ * into the end of the workspace, then run qmoe_layer on those ids and
+ * weights.  Workspace: qmoe_layer_logits_workspace_bytes; its first
+ * qmoe_layer_workspace_bytes bytes are the layer's workspace (worklist view
+ * as for qmoe_layer).  Limits are those of both calls (k <= 16, E <= 1024);
+ * logits may not overlap the workspace or out. */
+size_t qmoe_layer_logits_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
+                                         int32_t k, int32_t x_dtype);
+int qmoe_layer_logits(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+                      int32_t tokens, const float *logits, int32_t k, float *out, void *ws,
+                      size_t ws_bytes, void *stream);
+
 /* qmoe_layer with phase markers: when phase_events is non-NULL it holds
  * n_events hipEvent_t handles (passed as void*, created by the caller) and the
  * call records events[0] before its first kernel and events[i] after phase i

@@ -224,3 +224,21 @@ def test_cache_create_validation(lib):
     nul.up.q = None
     assert lib.qmoe_cache_create(ctypes.byref(nul), ctypes.byref(dev), ctypes.byref(h)) == 1
     assert lib.qmoe_cache_create(None, ctypes.byref(dev), ctypes.byref(h)) == 1
+
+
+def test_layer_logits_validation(lib):
+    d = layer_desc()
+    T, k = 2, 2
+    nb = lib.qmoe_layer_logits_workspace_bytes(ctypes.byref(d), T, k, 0)
+    assert nb >= lib.qmoe_layer_workspace_bytes(ctypes.byref(d), T, k, 0) + 2 * 256
+    X, L, O, W = FAKE + (60 << 32), FAKE + (61 << 32), FAKE + (62 << 32), FAKE + (63 << 32)
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L, 0, O, W, nb, None) == 2
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L, 17, O, W, nb, None) == 4
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, None, k, O, W, nb, None) == 1
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L + 2, k, O, W, nb, None) == 3
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L, k, O, W, nb - 16, None) == 5
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, W + 64, k, O, W, nb, None) == 6
+    # a bad layer argument is caught before the router would run
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, None, T, L, k, O, W, nb, None) == 1
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L, k, X, W, nb, None) == 6
+    assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, 0, None, k, None, None, 0, None) == 0

@@ -69,3 +69,21 @@ def test_route_feeds_layer():
     err = rel_l2(out, ref)
     say(f"  rel_l2 = {err:.3e}")
     assert err <= F32_TOL
+
+
+@pytest.mark.parametrize("dtype,T", [("f32", 9), ("bf16", 300)])
+def test_layer_logits_matches_route_then_layer(dtype, T):
+    say(f"layer from logits E=16 H=256 F=128 T={T} k=4 {dtype}")
+    L = Layer(16, 256, 128, seed=27)
+    g = synth.generator(28)
+    x = synth.rand_x(g, (T, 256))
+    if dtype == "bf16":
+        x = synth.to_bf16_rne(x)
+    logits = synth.normal_logits(g, T, 16)
+    out = qm.qmoe_layer_logits(L.dev, x.to(DEV), logits.to(DEV), 4).cpu().numpy()
+    rids, rw = orc().route(logits.numpy(), 4)
+    ref = L.oracle_layer(x.float() if dtype == "bf16" else x, torch.from_numpy(rids),
+                         torch.from_numpy(rw))
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else 2e-3)
