@@ -22,13 +22,17 @@
 //    the exact code, packed multiply by the f16 group scale), so the f32
 //    group scale costs no per-group accumulator work; rounding q*s to f16
 //    adds ~2^-12 relative error per weight (bf16 would be 2^-9).
-//  * v_mfma_f32_32x32x16_f16; block = 4 waves x (256 rows x 32 features of
-//    gate and of up) or 4 waves x (256 rows x 64 features) for down, so each
-//    unpacked weight fragment feeds 8 row fragments (accumulators live in
-//    AGPRs); row fragments past the tile's rows are skipped; the
-//    activation tile (128 x 64 f16 per group) is double-buffered in LDS with
-//    octets XOR-swizzled by row; global loads of group g+1 are issued
-//    before the MFMAs of group g, and two blocks per CU overlap waits.
+//  * v_mfma_f32_32x32x16_f16.  gate+up: block = 4 waves x (256 rows x 32
+//    features of gate and of up), so each unpacked weight fragment feeds 8
+//    row fragments (accumulators in AGPRs, one block per CU).  down
+//    (mfma_down.hip): block = 4 waves x (128 rows x 64 features), two blocks
+//    per CU.  A tile needing at most 1/2 or 1/4 of the block's rows runs a
+//    loop with that many row fragments.
+//  * The activation tile (rows x 64 f16 per group) reaches LDS by buffer
+//    loads that write LDS directly, into a 4-stage ring with octets
+//    XOR-swizzled by row; weights and scales run 4 groups ahead in
+//    registers; the main loop (mfma_loop.h) interleaves the next k-step's
+//    LDS reads and unpack with the current k-step's MFMAs.
 #include "mfma_loop.h"
 
 namespace qmoe {
