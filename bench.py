@@ -191,6 +191,108 @@ def time_router(qm, synth, torch, dev, reps=20):
     return res
 
 
+def expert_bytes(group):
+    """Packed codes + f32 scales of one expert (gate, up, down) for a group size."""
+    return 2 * (F * H // 2 + F * (-(-H // group)) * 4) + (H * F // 2 + H * (-(-F // group)) * 4)
+
+
+def time_formats(qm, synth, torch, dev, calls=16, reps=3):
+    """The same decode (16 tokens) and prefill (8192 tokens) layers with group
+    sizes 32 and 128 instead of 64: fresh weights per group size, decode
+    calls captured in a graph, prefill timed with events.  Not part of the
+    step."""
+    res = {}
+    for group in (32, 128):
+        g = synth.generator(3 + group, dev)
+        w = synth.layer_weights(g, E, H, F, device=dev, group=group)
+        pk = {k: qm.qmoe_pack(w[k]) for k in ("qg", "qu", "qd")}
+        layer = qm.QLayer(pk["qg"], w["sg"], pk["qu"], w["su"], pk["qd"], w["sd"], H, F,
+                          group=group)
+        del g
+        # decode, 16 tokens
+        wl = synth.LAYERS["decode_e128_t16"]
+        gen = synth.generator(wl.seed + 3000)
+        dec, nbytes = [], 0
+        for _ in range(calls):
+            x, ids, wt = synth.layer_inputs(wl, gen)
+            uniq = len(set(int(e) for e in ids.flatten().tolist() if 0 <= int(e) < E))
+            nbytes += uniq * expert_bytes(group) + 16 * H * 4 * 2 + 16 * K * 8
+            dec.append((x.to(dev), ids.to(dev), wt.to(dev), torch.empty(16, H, device=dev)))
+        wsd = torch.empty(layer.workspace_bytes(16, K, qm.QMOE_F32), dtype=torch.uint8,
+                          device=dev)
+
+        def run_dec():
+            for x, ids, wt, o in dec:
+                qm.qmoe_layer(layer, x, ids, wt, out=o, ws=wsd)
+        run_dec()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            run_dec()
+        graph.replay()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        del graph
+        # prefill, 8192 tokens
+        wlp = synth.LAYERS["prefill_e128_t8192"]
+        xp, ip, wp = synth.layer_inputs(wlp, synth.generator(wlp.seed))
+        pairs = int(((ip >= 0) & (ip < E)).sum())
+        xp, ip, wp = xp.to(dev), ip.to(dev), wp.to(dev)
+        op = torch.empty(PREFILL_T, H, device=dev)
+        wsp = torch.empty(layer.workspace_bytes(PREFILL_T, K, qm.QMOE_BF16), dtype=torch.uint8,
+                          device=dev)
+        qm.qmoe_layer(layer, xp, ip, wp, out=op, ws=wsp)
+        pbest = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            qm.qmoe_layer(layer, xp, ip, wp, out=op, ws=wsp)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            pbest = ms if pbest is None else min(pbest, ms)
+        flops = 2.0 * pairs * 3 * H * F
+        res[f"group{group}"] = {
+            "decode_t16_us_per_call": round(best * 1e3 / calls, 1),
+            "decode_t16_GBps": round(nbytes / (best * 1e-3) / 1e9, 1),
+            "decode_t16_frac_of_hbm_roofline": round(nbytes / HBM_PEAK / (best * 1e-3), 4),
+            "prefill_t8192_ms": round(pbest, 4),
+            "prefill_t8192_TFLOPs": round(flops / (pbest * 1e-3) / 1e12, 1),
+            "prefill_t8192_frac_of_mfma_roofline": round(flops / BF16_PEAK / (pbest * 1e-3), 4),
+        }
+        del layer, pk, w, wsd, wsp
+        torch.cuda.empty_cache()
+    # two's-complement import of one full gate stack (E x F rows of H/2 bytes)
+    tw = torch.randint(0, 256, (E * F, H // 2), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(tw)
+    qm.qmoe_import_twos(tw, H, out=out)
+    ibest = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        qm.qmoe_import_twos(tw, H, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        ibest = ms if ibest is None else min(ibest, ms)
+    nb = 2 * tw.numel()
+    res["import_twos"] = {"bytes": nb, "ms": round(ibest, 4),
+                          "GBps": round(nb / (ibest * 1e-3) / 1e9, 1),
+                          "frac_of_hbm_roofline": round(nb / HBM_PEAK / (ibest * 1e-3), 4)}
+    del tw, out
+    return res
+
+
 PCIE_PEAK = 64.0e9     # B/s, host link of one MI355X (PCIe 5.0 x16, one direction)
 
 
@@ -474,6 +576,7 @@ def main():
     }
     rec["router"] = time_router(qm, synth, torch, dev)
     rec["host_experts"] = time_host_experts(qm, synth, torch, dev, replicas[0])
+    rec["group_sizes"] = time_formats(qm, synth, torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         log("timing the CPU oracle on a bounded sample ...")
