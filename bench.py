@@ -370,6 +370,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="time only part of the step (for counter runs)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the router, host-expert and group-size timings that run "
+                         "after the step (for profiler runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times and exit "
                          "(reference for HBM byte counters)")
@@ -574,9 +577,10 @@ def main():
             "avg_launch_ms": round(gateup_ms, 4),
         },
     }
-    rec["router"] = time_router(qm, synth, torch, dev)
-    rec["host_experts"] = time_host_experts(qm, synth, torch, dev, replicas[0])
-    rec["group_sizes"] = time_formats(qm, synth, torch, dev)
+    if not args.no_extras:
+        rec["router"] = time_router(qm, synth, torch, dev)
+        rec["host_experts"] = time_host_experts(qm, synth, torch, dev, replicas[0])
+        rec["group_sizes"] = time_formats(qm, synth, torch, dev)
     if not args.no_cpu_baseline:
         import oracle
         log("timing the CPU oracle on a bounded sample ...")
