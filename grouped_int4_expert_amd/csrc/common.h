@@ -109,4 +109,64 @@ __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
     return factor;
 }
 
+// Dot of one 32-element chunk: weights w[0..3] (two's-complement nibbles)
+// against the five digit planes at x[0..19].
+__device__ __forceinline__ float chunk_dot(const uint32_t *w, const uint32_t *x, float fac) {
+    int s[XD_PLANES];
+#pragma unroll
+    for (int k = 0; k < XD_PLANES; k++) {
+        int a = 0;
+#pragma unroll
+        for (int d = 0; d < 4; d++) a = sdot8(w[d], x[4 * k + d], a);
+        s[k] = a;
+    }
+    int v = s[4];
+#pragma unroll
+    for (int k = 3; k >= 0; k--) v = v * 16 + s[k];
+    return (float)v * fac;
+}
+
+// Sum over groups of LPR consecutive lanes (LPR = 8, 16, 32 or 64) with DPP
+// row shifts and row broadcasts (VALU only); the sum is valid in the last
+// lane of each group.
+__device__ __forceinline__ float dpp_add(float v, int t) { return v + __int_as_float(t); }
+template <int LPR>
+__device__ __forceinline__ float reduce_dpp(float v) {
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
+    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
+    if (LPR >= 16)
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
+    if (LPR >= 32)   // row_bcast:15 into rows 1 and 3
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    if (LPR >= 64)   // row_bcast:31 into rows 2 and 3
+        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer loads.  A descriptor (base, byte size) lives in scalar registers and
+// each lane supplies a 32-bit byte offset; bytes past the size read as zero.
+// Where a lane is switched off with OOB_OFFSET, the descriptor covers less
+// than 2^31 bytes and the other offsets of the access stay below 2^31, so
+// the sum stays out of range.
+// ---------------------------------------------------------------------------
+constexpr uint32_t OOB_OFFSET = 0x80000000u;
+
+// Word 3 selects the 32-bit data format that raw loads require.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(uint32_t)bytes, 0x00020000);
+}
+
+// An LDS pointer as the address-space-3 pointer that loads writing LDS take.
+#define QMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt immediate (gfx9 layout) that waits until at most n (< 64) vector
+// memory operations of this wave are outstanding and leaves the other
+// counters alone.
+__host__ __device__ constexpr int waitcnt_vm(int n) {
+    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 }  // namespace qmoe

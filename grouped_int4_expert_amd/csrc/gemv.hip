@@ -71,23 +71,6 @@ __device__ __forceinline__ void load_digits(XReg<GPL> &xr, const XDigits &xd, in
     }
 }
 
-// Dot of one 32-element chunk: weights w[0..3] (two's-complement nibbles)
-// against the five digit planes at x[0..19].
-__device__ __forceinline__ float chunk_dot(const uint32_t *w, const uint32_t *x, float fac) {
-    int s[XD_PLANES];
-#pragma unroll
-    for (int k = 0; k < XD_PLANES; k++) {
-        int a = 0;
-#pragma unroll
-        for (int d = 0; d < 4; d++) a = sdot8(w[d], x[4 * k + d], a);
-        s[k] = a;
-    }
-    int v = s[4];
-#pragma unroll
-    for (int k = 3; k >= 0; k--) v = v * 16 + s[k];
-    return (float)v * fac;
-}
-
 template <int GPL, int U>
 struct WReg {
     uint32_t w[U][GPL][8];
@@ -106,12 +89,6 @@ struct RowSrc {
     uint32_t rb, sb;     // packed bytes and scale bytes per row
 };
 
-constexpr uint32_t OOB_OFFSET = 0x80000000u;   // > any descriptor size used here
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                             (int)(uint32_t)bytes, 0x00020000);
-}
 
 template <int GPL, int LPR, bool G32>
 __device__ __forceinline__ RowSrc<GPL> row_src(const QMat &M, int e, int lr) {
@@ -119,8 +96,8 @@ __device__ __forceinline__ RowSrc<GPL> row_src(const QMat &M, int e, int lr) {
     const int ng = M.cols / 64;
     r.rb = (uint32_t)(M.cols / 2);
     r.sb = (uint32_t)scales_per_row(M) * 4;
-    r.q = gv_rsrc(M.q + (int64_t)e * M.q_stride, (int64_t)M.rows * r.rb);
-    r.s = gv_rsrc(M.s + (int64_t)e * M.s_stride, (int64_t)M.rows * r.sb);
+    r.q = make_rsrc(M.q + (int64_t)e * M.q_stride, (int64_t)M.rows * r.rb);
+    r.s = make_rsrc(M.s + (int64_t)e * M.s_stride, (int64_t)M.rows * r.sb);
 #pragma unroll
     for (int gi = 0; gi < GPL; gi++) {
         const int g = lr + gi * LPR;
@@ -205,25 +182,6 @@ __device__ __forceinline__ bool block_expert(const GemvRoute &r, int a, int &e, 
 
 __device__ __forceinline__ int64_t token_of(const GemvRoute &r, int pos) {
     return r.rec == nullptr ? pos : r.tok[pos];
-}
-
-// Sum over groups of LPR consecutive lanes with DPP row shifts and row
-// broadcasts (VALU only); the sum is valid in the last lane of each group.
-__device__ __forceinline__ float dpp_add(float v, int t) { return v + __int_as_float(t); }
-template <int LPR>
-__device__ __forceinline__ float reduce_dpp(float v) {
-    const int vi = 0;
-    (void)vi;
-    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, false));
-    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, false));
-    v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, false));
-    if (LPR >= 16)
-        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, false));
-    if (LPR >= 32)   // row_bcast:15 into rows 1 and 3
-        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
-    if (LPR >= 64)   // row_bcast:31 into rows 2 and 3
-        v = dpp_add(v, __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
-    return v;
 }
 
 // Rows per batch: about 128 bytes of weights in flight per lane per batch.

@@ -26,12 +26,6 @@ constexpr int DOWN_BM = 128;
 // LDS offset (in 16-bit elements) of octet `o` of row `m` in a BMK x 64 tile.
 __device__ __forceinline__ int sw_off(int m, int o) { return m * 64 + ((o ^ (m & 7)) << 3); }
 
-// s_waitcnt immediate (gfx9 layout) that waits until at most n vector memory
-// loads of this wave are outstanding and leaves the other counters alone.
-__host__ __device__ constexpr int waitcnt_vm(int n) {
-    return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
-}
-
 // Position of element e (0..7) of an octet after the unpack permutation.
 __device__ __forceinline__ int octet_pos(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
 
@@ -144,13 +138,6 @@ struct Frags {
     f32x16 acc[MF][NF];
 };
 
-// Buffer descriptor over [base, base + bytes); bytes < 2^32 is checked by
-// the host.  Word 3 selects 32-bit data format, as raw loads require.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                             (int)(uint32_t)bytes, 0x00020000);
-}
-
 // Sources of one block: activation tile (one descriptor, MF lane offsets at
 // group 0) and the wave's two weight column fragments.
 template <int MF>
@@ -166,8 +153,6 @@ struct LoopSrc {
     uint32_t qoff[NF], soff[NF];
     int gshift;
 };
-
-#define QMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Scheduling hint for one k-step: n_mfma MFMAs, each followed by one LDS
 // read (while any remain) and `valu` VALU instructions.
