@@ -221,11 +221,38 @@ int qmoe_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q, vo
     return status_of(launch_unpack(packed, rows, cols, q, as_stream(stream)));
 }
 
+// A matvec over a width that is not a multiple of 64 (a partial last group)
+// runs on a copy of W re-laid to the next multiple of 64 in the workspace:
+// the added columns hold code 0 and the added groups scale 0, and x is read
+// as zero past its width.  Group 32 and 64 * 2^j keep their scale index;
+// one scale per row (group >= cols) becomes group = padded width.
+struct MatvecPlan {
+    int64_t cols;       // padded width
+    int64_t group;      // group of the padded matrix
+    int64_t ng_in, ng;  // scales per row before and after
+    bool relaid;
+};
+
+static MatvecPlan matvec_plan(const qmoe_qmat *W) {
+    MatvecPlan p;
+    p.cols = (W->cols + 63) / 64 * 64;
+    p.relaid = p.cols != W->cols;
+    p.group = W->group >= W->cols ? p.cols : W->group;
+    p.ng_in = (W->cols + W->group - 1) / W->group;
+    p.ng = (p.cols + p.group - 1) / p.group;
+    return p;
+}
+
 size_t qmoe_matvec_workspace_bytes(const qmoe_qmat *W, int32_t batch) {
-    if (!W || batch < 0 || W->cols <= 0) return 0;
+    if (!W || batch < 0 || W->cols <= 0 || W->rows <= 0 || W->group <= 0) return 0;
+    const MatvecPlan p = matvec_plan(W);
     Carver c(nullptr);
-    c.take<uint32_t>((int64_t)batch * (W->cols / 32) * 20);
-    c.take<float>((int64_t)batch * (W->cols / 32));
+    c.take<uint32_t>((int64_t)batch * (p.cols / 32) * 20);
+    c.take<float>((int64_t)batch * (p.cols / 32));
+    if (p.relaid) {
+        c.take<uint8_t>((int64_t)W->rows * (p.cols / 2));
+        c.take<float>((int64_t)W->rows * p.ng);
+    }
     return (size_t)c.off;
 }
 
@@ -234,9 +261,11 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     if (!W) return QMOE_ERR_NULL;
     if (W->struct_size != sizeof(qmoe_qmat)) return QMOE_ERR_ABI;
     if (batch < 0 || W->rows <= 0 || W->cols <= 0 || W->group <= 0) return QMOE_ERR_SHAPE;
-    int s = check_qmat(W, W->rows, W->cols, 1);
-    if (s) return s;
-    if (!gemv_supported(W->cols)) return QMOE_ERR_UNSUPPORTED;
+    if (!group_supported(W->group, W->cols)) return QMOE_ERR_UNSUPPORTED;
+    const MatvecPlan p = matvec_plan(W);
+    if (!gemv_supported((int)p.cols)) return QMOE_ERR_UNSUPPORTED;
+    if (!W->q || !W->s) return QMOE_ERR_NULL;
+    if (!aligned16(W->q) || !aligned16(W->s)) return QMOE_ERR_ALIGN;
     if (batch == 0) return QMOE_OK;
     if (!x || !y) return QMOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_ALIGN;
@@ -246,15 +275,28 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     const int64_t xb = (int64_t)batch * W->cols * 4, yb = (int64_t)batch * W->rows * 4;
     if (overlap(y, yb, x, xb) || overlap(y, yb, ws, need) || overlap(x, xb, ws, need) ||
         overlap(y, yb, W->q, packed_bytes(W->rows, W->cols)) ||
-        overlap(y, yb, W->s, 4 * scale_count(W->rows, W->cols, W->group)))
+        overlap(y, yb, W->s, 4 * scale_count(W->rows, W->cols, W->group)) ||
+        overlap(ws, need, W->q, packed_bytes(W->rows, W->cols)) ||
+        overlap(ws, need, W->s, 4 * scale_count(W->rows, W->cols, W->group)))
         return QMOE_ERR_ALIAS;
     Carver c(ws);
     XDigits xd;
-    xd.dig = c.take<uint32_t>((int64_t)batch * (W->cols / 32) * 20);
-    xd.fac = c.take<float>((int64_t)batch * (W->cols / 32));
+    xd.dig = c.take<uint32_t>((int64_t)batch * (p.cols / 32) * 20);
+    xd.fac = c.take<float>((int64_t)batch * (p.cols / 32));
     const hipStream_t st = as_stream(stream);
-    hipError_t e = launch_xdigits(x, batch, W->cols, xd, st);
-    if (e == hipSuccess) e = launch_gemv_matvec(to_qmat(W), xd, batch, y, st);
+    QMat M = to_qmat(W);
+    hipError_t e = hipSuccess;
+    if (p.relaid) {
+        uint8_t *q2 = c.take<uint8_t>((int64_t)W->rows * (p.cols / 2));
+        float *s2 = c.take<float>((int64_t)W->rows * p.ng);
+        e = launch_pad_cols(W->q, W->s, W->rows, W->cols, p.ng_in, q2, p.cols, s2, p.ng, st);
+        M.q = q2;
+        M.s = s2;
+        M.cols = (int)p.cols;
+        M.group = (int)p.group;
+    }
+    if (e == hipSuccess) e = launch_xdigits(x, batch, (int)p.cols, W->cols, xd, st);
+    if (e == hipSuccess) e = launch_gemv_matvec(M, xd, batch, y, st);
     return status_of(e);
 }
 
@@ -318,7 +360,7 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
         GemvRoute r{};
         r.ntok = batch;
         r.batch_tokens = batch;
-        e = launch_xdigits(static_cast<const float *>(x), batch, H, xd, st);
+        e = launch_xdigits(static_cast<const float *>(x), batch, H, H, xd, st);
         if (e == hipSuccess) e = launch_gemv_gateup(to_qmat(gate), to_qmat(up), xd, hd, r, st);
         if (e == hipSuccess) e = launch_gemv_down(to_qmat(down), hd, out, r, st);
     } else {

@@ -57,6 +57,11 @@ hipError_t launch_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, u
                               hipStream_t st);
 hipError_t launch_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
                          hipStream_t st);
+// Re-lay a matrix of `cols` inputs as one of cols_out inputs (code 0 and
+// scale 0 in the added columns and groups).
+hipError_t launch_pad_cols(const uint8_t *q, const float *s, int64_t rows, int64_t cols, int64_t ng,
+                           uint8_t *qo, int64_t cols_out, float *so, int64_t ng_out,
+                           hipStream_t st);
 
 // Worklist for n = tokens*k pairs.  block_counts: scratch of
 // wl_scratch_ints(n, E) int32 (unused when n is small).
@@ -82,8 +87,11 @@ hipError_t launch_decode_prep(const int32_t *ids, const float *topk_w, int n, in
                               const Worklist &wl, const DecodePlan &plan, const float *x,
                               int tokens, int hidden, XDigits xd, float *out, hipStream_t st);
 
-// x -> digits only (matvec and the single-expert FFN).
-hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStream_t st);
+// x -> digits only (matvec and the single-expert FFN): rows of `cols`
+// digits (a multiple of 32) from x rows of src_cols <= cols elements, the
+// elements past src_cols taken as 0.
+hipError_t launch_xdigits(const float *x, int rows, int cols, int src_cols, XDigits xd,
+                          hipStream_t st);
 
 // Decode GEMVs.  Tokens of expert `active[a]` are the sorted positions
 // offsets[e]..offsets[e+1]; in "direct" mode (wl.pairs == nullptr) there is

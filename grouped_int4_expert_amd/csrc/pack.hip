@@ -69,6 +69,28 @@ __global__ void import_twos_kernel(const uint8_t *twos, int64_t n, uint8_t *pack
     for (int64_t j = done + i; j < n; j += stride) packed[j] = (uint8_t)(twos[j] ^ 0x88u);
 }
 
+// Re-lay a matrix of `cols` inputs (rows of ceil(cols/2) packed bytes, ng
+// scales) as one of cols_out >= cols inputs (cols_out/2 bytes per row, ng_out
+// >= ng scales): the added nibbles are 8 (code 0) and the added scales 0, so
+// every added column contributes nothing.  Byte-wise: a row of the input may
+// start at any byte.
+__global__ void pad_cols_kernel(const uint8_t *__restrict__ q, const float *__restrict__ s,
+                                int64_t rows, int64_t cols, int64_t ng, uint8_t *__restrict__ qo,
+                                int64_t cols_out, float *__restrict__ so, int64_t ng_out) {
+    const int64_t rb = (cols + 1) / 2, rbo = cols_out / 2;
+    const int64_t nq = rows * rbo, n = nq + rows * ng_out;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < nq) {
+            const int64_t r = i / rbo, b = i - r * rbo;
+            qo[i] = b < rb ? q[r * rb + b] : (uint8_t)0x88;
+        } else {
+            const int64_t j = i - nq, r = j / ng_out, c = j - r * ng_out;
+            so[j] = c < ng ? s[r * ng + c] : 0.0f;
+        }
+    }
+}
+
 __global__ void zero_i32_kernel(int32_t *p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -107,6 +129,15 @@ hipError_t launch_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, u
                      15u) == 0;
     hipLaunchKernelGGL(import_twos_kernel, dim3(grid_for(vec ? n / 16 + 1 : n, 256)), dim3(256),
                        0, st, twos, n, packed, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_pad_cols(const uint8_t *q, const float *s, int64_t rows, int64_t cols, int64_t ng,
+                           uint8_t *qo, int64_t cols_out, float *so, int64_t ng_out,
+                           hipStream_t st) {
+    const int64_t n = rows * (cols_out / 2 + ng_out);
+    hipLaunchKernelGGL(pad_cols_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, q, s, rows, cols,
+                       ng, qo, cols_out, so, ng_out);
     return hipGetLastError();
 }
 }  // namespace qmoe

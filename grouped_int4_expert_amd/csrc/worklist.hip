@@ -207,15 +207,16 @@ hipError_t launch_worklist(const int32_t *ids, int n, int k, int E, const Workli
 // ---------------------------------------------------------------------------
 // Activation digits (see common.h).  One 32-lane half-wave per chunk.
 // ---------------------------------------------------------------------------
-__device__ void xdigits_chunks(const float *__restrict__ x, int rows, int cols, XDigits xd,
-                               int64_t first_half, int64_t stride_halves) {
+__device__ void xdigits_chunks(const float *__restrict__ x, int rows, int cols, int src_cols,
+                               XDigits xd, int64_t first_half, int64_t stride_halves) {
     const int cpr = cols / XD_CHUNK;
     const int64_t nchunks = (int64_t)rows * cpr;
     const int half = (threadIdx.x >> 5);
     const int sub = threadIdx.x & 31;
     for (int64_t c = first_half + half; c < nchunks; c += stride_halves) {
         const int64_t r = c / cpr, ch = c - r * cpr;
-        const float v = x[r * cols + ch * XD_CHUNK + sub];
+        const int e = (int)ch * XD_CHUNK + sub;
+        const float v = e < src_cols ? x[r * src_cols + e] : 0.0f;
         uint32_t *dst = xd.dig + c * XD_DWORDS;
         const float f = quantise_chunk32(v, [&](int plane, int dw, uint32_t val) {
             dst[plane * 4 + dw] = val;
@@ -225,17 +226,19 @@ __device__ void xdigits_chunks(const float *__restrict__ x, int rows, int cols, 
 }
 
 __global__ void __launch_bounds__(256) xdigits_kernel(const float *__restrict__ x, int rows,
-                                                      int cols, XDigits xd) {
+                                                      int cols, int src_cols, XDigits xd) {
     const int64_t halves_per_block = blockDim.x / 32;
-    xdigits_chunks(x, rows, cols, xd, (int64_t)blockIdx.x * halves_per_block,
+    xdigits_chunks(x, rows, cols, src_cols, xd, (int64_t)blockIdx.x * halves_per_block,
                    (int64_t)gridDim.x * halves_per_block);
 }
 
-hipError_t launch_xdigits(const float *x, int rows, int cols, XDigits xd, hipStream_t st) {
+hipError_t launch_xdigits(const float *x, int rows, int cols, int src_cols, XDigits xd,
+                          hipStream_t st) {
     const int64_t nchunks = (int64_t)rows * (cols / XD_CHUNK);
     int64_t g = (nchunks + 7) / 8;
     if (g > 4096) g = 4096;
-    hipLaunchKernelGGL(xdigits_kernel, dim3((int)g), dim3(256), 0, st, x, rows, cols, xd);
+    hipLaunchKernelGGL(xdigits_kernel, dim3((int)g), dim3(256), 0, st, x, rows, cols, src_cols,
+                       xd);
     return hipGetLastError();
 }
 
@@ -350,7 +353,7 @@ __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
     const int64_t hpb = blockDim.x / 32;
     const int64_t first = (int64_t)(blockIdx.x - 1) * hpb;
     const int64_t stride = (int64_t)(gridDim.x - 1) * hpb;
-    xdigits_chunks(x, tokens, hidden, xd, first, stride);
+    xdigits_chunks(x, tokens, hidden, hidden, xd, first, stride);
     const int64_t total = (int64_t)tokens * hidden;
     for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)(gridDim.x - 1) * blockDim.x)

@@ -32,11 +32,14 @@
  *    gives two's complement).  Scales are row-major f32 [rows][ceil(cols/g)]
  *    with scale(o, i) = s[o * ng + i / g] (comment "blocked by GPU driver
  *    instability": scales[o*ng + i/gs]).
- *  - GPU kernels accept group == 64 and cols % 64 == 0 only; other values
- *    return QMOE_ERR_UNSUPPORTED.  Every pointer must be 16-byte aligned
- *    (QMOE_ERR_ALIGN otherwise), like the vector-load guard of the
- *    pxq_llama.cpp notes (release rc3 fixes) that declines rather than
- *    faults.
+ *  - Group sizes: 32, 64 * 2^j, or any group >= cols (one scale per row, the
+ *    per-row int4 format); others return QMOE_ERR_UNSUPPORTED.  The layer
+ *    and expert-FFN entry points take widths (hidden, inter) that are
+ *    multiples of 64, as every MoE shape on the pages is; qmoe_matvec takes
+ *    any width, a partial last group included.  Every pointer must be
+ *    16-byte aligned (QMOE_ERR_ALIGN otherwise), like the vector-load guard
+ *    of the pxq_llama.cpp notes (release rc3 fixes) that declines rather
+ *    than faults.
  *  - Bad expert ids (outside [0, E)) are data, not arguments: they are
  *    dropped (contribute zero) and counted into an int32 on the device.
  */
@@ -126,13 +129,22 @@ int qmoe_pack(const int8_t *q, int64_t rows, int64_t cols, uint8_t *packed,
 int qmoe_unpack(const uint8_t *packed, int64_t rows, int64_t cols, int8_t *q,
                 void *stream);
 
-/* Workspace bytes qmoe_matvec needs for `batch` rows of x. */
+/* Workspace bytes qmoe_matvec needs for `batch` rows of x (0 for an invalid
+ * descriptor).  When cols is not a multiple of 64 this includes a re-laid
+ * copy of W (rows * cols64 / 2 bytes and its scales, cols64 = cols rounded
+ * up to 64). */
 size_t qmoe_matvec_workspace_bytes(const qmoe_qmat *W, int32_t batch);
 
-/* y[b][o] = sum_i s[o][i/64] * q[o][i] * x[b][i] for b < batch: the single
+/* y[b][o] = sum_i s[o][i/g] * q[o][i] * x[b][i] for b < batch: the single
  * grouped int4 matvec ("quant_matmul" with per-group scale, pull request
- * Summary).  x f32 [batch][cols], y f32 [batch][rows]; y must not overlap x
- * or the workspace.  W->q_expert_stride is ignored (expert 0). */
+ * Summary).  x f32 [batch][cols], y f32 [batch][rows]; y must not overlap x,
+ * W or the workspace, and the workspace must not overlap W.
+ * W->q_expert_stride is ignored (expert 0).  Any cols >= 1, odd widths and a
+ * last group shorter than g included (shapes the pull request's comment
+ * that adds a double-precision C test for the grouped kernel covers): W is
+ * then first re-laid in the workspace to a width that is a multiple of 64,
+ * the added columns holding code 0 and the added groups scale 0, and x is
+ * read as zero past cols. */
 int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y,
                 void *ws, size_t ws_bytes, void *stream);
 

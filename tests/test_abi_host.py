@@ -129,8 +129,18 @@ def test_matvec_and_pack_rejections(lib):
     nb = lib.qmoe_matvec_workspace_bytes(ctypes.byref(W), 1)
     assert nb > 0
     ws = FAKE + (20 << 32)
-    assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1000)), FAKE, 1, FAKE + (30 << 32), ws, nb,
-                           None) == 4
+    # a width that is not a multiple of 64 (partial last group) is taken, with
+    # a re-laid copy of W in the workspace: rows * 1024/2 bytes + 16 scales
+    Wp = qmat(256, 1000)
+    nbp = lib.qmoe_matvec_workspace_bytes(ctypes.byref(Wp), 1)
+    assert nbp >= nb + 256 * 512 + 256 * 16 * 4
+    assert lib.qmoe_matvec(ctypes.byref(Wp), FAKE, 1, FAKE + (30 << 32), ws, nb, None) == 5
+    assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1000, q_=ws + 4096)), FAKE + (40 << 32), 1,
+                           FAKE + (30 << 32), ws, nbp, None) == 6      # workspace overlaps W
+    assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1000, group=96)), FAKE, 1, FAKE + (30 << 32),
+                           ws, nbp, None) == 4
+    assert lib.qmoe_matvec(ctypes.byref(qmat(4, 20000)), FAKE, 1, FAKE + (30 << 32), ws,
+                           1 << 30, None) == 4                            # wider than any shape
     assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1024, size=3)), FAKE, 1, FAKE, ws, nb,
                            None) == 7
     assert lib.qmoe_matvec(ctypes.byref(W), None, 1, FAKE + (30 << 32), ws, nb, None) == 1

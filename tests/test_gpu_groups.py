@@ -81,3 +81,29 @@ def test_decode_layer_full_size_groups(group):
     err = rel_l2(out[toks], ref)
     say(f"  rel_l2 = {err:.3e}")
     assert err <= F32_TOL
+
+
+@pytest.mark.parametrize("group", [32, 64, 128, "row"])
+@pytest.mark.parametrize("cols", [1, 5, 31, 33, 63, 65, 100, 200, 1000, 4097])
+def test_matvec_partial_last_group(group, cols):
+    # widths that are not a multiple of 64 (odd widths, a last group shorter
+    # than the group size, a group wider than the row): W is re-laid in the
+    # workspace; random x against the oracle, one-hot x bit-exact
+    rows, batch = 37, 3
+    gs = _gs(group, cols)
+    say(f"partial-width matvec {rows}x{cols} group {gs}")
+    g = synth.generator(67 + cols)
+    q = synth.rand_q(g, (rows, cols))
+    s = synth.rand_scales(g, (rows, -(-cols // gs)))
+    x = synth.rand_x(g, (batch, cols))
+    pk = qm.qmoe_pack(q.to(DEV))
+    y = qm.qmoe_matvec(pk, s.to(DEV), cols, x.to(DEV), group=gs).cpu()
+    pq, _ = orc().pack(q.numpy())
+    ref = orc().matvec(pq, s.numpy(), cols, x.numpy(), gs=gs)
+    assert rel_l2(y.numpy(), ref) <= F32_TOL
+    for j in sorted({0, cols // 2, cols - 1}):
+        e = torch.zeros(1, cols)
+        e[0, j] = 1.0
+        y1 = qm.qmoe_matvec(pk, s.to(DEV), cols, e.to(DEV), group=gs).cpu()
+        exact = (q[:, j].to(torch.float64) * s[:, j // gs].to(torch.float64)).to(torch.float32)
+        assert torch.equal(y1[0], exact), (j, float((y1[0] - exact).abs().max()))
