@@ -205,7 +205,8 @@ def qmoe_unpack(packed: torch.Tensor, cols: int, stream=None):
 # ------------------------------------------------------------ descriptors ---
 
 def make_qmat(q: torch.Tensor, s: torch.Tensor, cols: int, group: int = 64) -> qmoe_qmat:
-    """Descriptor of packed codes q [E?, rows, cols/2] and scales s [E?, rows, ng]."""
+    """Descriptor of packed codes q [E?, rows, ceil(cols/2)] and scales
+    s [E?, rows, ceil(cols/group)]."""
     rows = q.shape[-2]
     m = qmoe_qmat()
     m.struct_size = ctypes.sizeof(qmoe_qmat)
@@ -218,10 +219,10 @@ def make_qmat(q: torch.Tensor, s: torch.Tensor, cols: int, group: int = 64) -> q
 
 
 class QLayer:
-    """Stacked int4-g64 weights of one MoE layer resident on the device.
+    """Stacked grouped-int4 weights of one MoE layer resident on the device.
 
-    gate/up packed [E, F, H/2] + scales [E, F, H/64]; down packed [E, H, F/2]
-    + scales [E, H, F/64]."""
+    gate/up packed [E, F, H/2] + scales [E, F, ceil(H/group)]; down packed
+    [E, H, F/2] + scales [E, H, ceil(F/group)]."""
 
     def __init__(self, pg, sg, pu, su, pd, sd, hidden, inter, group=64):
         self.tensors = [pg, sg, pu, su, pd, sd]
@@ -328,7 +329,8 @@ def _workspace(nbytes, device, ws):
 # ------------------------------------------------------------------ calls ---
 
 def qmoe_matvec(pq, s, cols, x, group=64, out=None, ws=None, stream=None):
-    """y = W x; W packed [rows, cols/2] + scales [rows, ng]; x f32 [B, cols]."""
+    """y = W x; W packed [rows, ceil(cols/2)] + scales [rows, ceil(cols/group)];
+    x f32 [B, cols].  Any cols (a partial last group is re-laid on the device)."""
     _dev(x, "x", torch.float32)
     W = make_qmat(pq, s, cols, group)
     batch = x.shape[0] if x.dim() == 2 else 1

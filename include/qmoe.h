@@ -72,7 +72,7 @@ enum {
  * kernels), bf16 = prefill (grouped MFMA kernels). */
 enum { QMOE_F32 = 0, QMOE_BF16 = 1 };
 
-/* One int4-g64 matrix, or a stack of per-expert matrices of one shape.
+/* One grouped int4 matrix, or a stack of per-expert matrices of one shape.
  * q_expert_stride is the byte distance between experts' packed codes and
  * s_expert_stride the float distance between their scales (0 for a single
  * matrix).  Both must keep every expert 16-byte aligned. */
@@ -80,9 +80,9 @@ typedef struct qmoe_qmat {
     uint32_t struct_size;     /* = sizeof(qmoe_qmat) */
     int32_t rows;             /* O: output features */
     int32_t cols;             /* I: input features */
-    int32_t group;            /* g: inputs per scale (64) */
-    const uint8_t *q;         /* packed codes, [E][rows][cols/2] bytes */
-    const float *s;           /* scales, [E][rows][cols/group] f32 */
+    int32_t group;            /* g: inputs per scale (64 on the pages) */
+    const uint8_t *q;         /* packed codes, [E][rows][ceil(cols/2)] bytes */
+    const float *s;           /* scales, [E][rows][ceil(cols/group)] f32 */
     int64_t q_expert_stride;  /* bytes between experts */
     int64_t s_expert_stride;  /* floats between experts */
 } qmoe_qmat;
@@ -94,7 +94,7 @@ typedef struct qmoe_layer_desc {
     int32_t experts;          /* E, 1..1024 */
     int32_t hidden;           /* H */
     int32_t inter;            /* F */
-    int32_t group;            /* 64 */
+    int32_t group;            /* inputs per scale, = each matrix's group */
     qmoe_qmat gate, up, down;
 } qmoe_layer_desc;
 
