@@ -301,6 +301,39 @@ def test_layer_all_ids_invalid_gives_zero(dtype):
     assert torch.count_nonzero(out).item() == 0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_max_experts(dtype):
+    """E = 1024 (the largest expert count): most experts get one pair or none."""
+    say(f"layer E=1024 H=256 F=128 T=60 k=8 {dtype}")
+    L = Layer(1024, 256, 128, seed=35)
+    out, ref = _layer_case(L, 60, 8, dtype, seed=36)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("dtype,T", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("f32", 2)])
+def test_layer_tiny_batches(dtype, T):
+    """A handful of tokens, including the MFMA path with single-row tiles."""
+    say(f"layer E=16 H=512 F=256 T={T} k=4 {dtype}")
+    L = Layer(16, 512, 256, seed=37)
+    out, ref = _layer_case(L, T, 4, dtype, seed=38 + T)
+    assert rel_l2(out, ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("H,F", [(512, 1024), (1536, 512)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_other_aspect_ratios(H, F, dtype):
+    """Intermediate wider than hidden and the reverse, beside the 4096/1536
+    and 6144/2048 shapes."""
+    say(f"layer E=8 H={H} F={F} T=33 k=2 {dtype}")
+    L = Layer(8, H, F, seed=39)
+    out, ref = _layer_case(L, 33, 2, dtype, seed=40)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
 def test_layer_wide_topk():
     """k = 16 of 32 experts, f32 and bf16."""
     L = Layer(32, 256, 128, seed=33)
