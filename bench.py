@@ -191,6 +191,36 @@ def time_router(qm, synth, torch, dev, reps=20):
     return res
 
 
+def time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t, reps=3):
+    """The step's decode calls split by batch size: each batch size's calls
+    captured in a graph of their own and replayed.  Not part of the step."""
+    res = {}
+    for T, calls in decode_dev.items():
+        def run():
+            for c in calls:
+                qm.qmoe_layer(c["layer"], c["x"], c["ids"], c["w"], out=c["out"], ws=c["ws"])
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            run()
+        graph.replay()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        del graph
+        res[f"t{T}"] = {"us_per_call": round(best * 1e3 / len(calls), 1),
+                        "GBps": round(bytes_by_t[T] / (best * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_roofline": round(bytes_by_t[T] / HBM_PEAK / (best * 1e-3), 4)}
+    return res
+
+
 def expert_bytes(group):
     """Packed codes + f32 scales of one expert (gate, up, down) for a group size."""
     return 2 * (F * H // 2 + F * (-(-H // group)) * 4) + (H * F // 2 + H * (-(-F // group)) * 4)
@@ -425,13 +455,16 @@ def main():
     roof_step += (MATVEC[0] * MATVEC[1] // 2 + MATVEC[0] * MATVEC[1] // 64 * 4 +
                   MATVEC[1] * 4 + MATVEC[0] * 4) / HBM_PEAK
     dec_bytes += MATVEC[0] * MATVEC[1] // 2 + MATVEC[0] * MATVEC[1] // 64 * 4 + MATVEC[1] * 8
+    bytes_by_t = {}
     for T in DECODE_T:
         wl = synth.LAYERS[f"decode_e128_t{T}"]
         gen = synth.generator(wl.seed)
         decode_inputs[T], decode_dev[T] = [], []
+        bytes_by_t[T] = 0
         for i in range(CALLS):
             x, ids, w = synth.layer_inputs(wl, gen)
             nb, fl, rt = decode_alg(ids, T)
+            bytes_by_t[T] += nb
             dec_bytes += nb
             dec_flops += fl
             roof_step += rt
@@ -578,6 +611,7 @@ def main():
         },
     }
     if not args.no_extras:
+        rec["decode"]["by_tokens"] = time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t)
         rec["router"] = time_router(qm, synth, torch, dev)
         rec["host_experts"] = time_host_experts(qm, synth, torch, dev, replicas[0])
         rec["group_sizes"] = time_formats(qm, synth, torch, dev)
