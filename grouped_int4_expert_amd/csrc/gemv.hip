@@ -284,8 +284,17 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false, G32>(
     }
 }
 
+// Output rows per down block: 64 for one group per lane, fewer for wider
+// rows (32 at two groups, 16 at three), whose fully unrolled 64-row stream
+// would not fit the register file; at least one row per lane group.
+__host__ __device__ constexpr int down_rows_per_block(int gpl, int lpr) {
+    const int base = gpl >= 3 ? 16 : gpl == 2 ? 32 : 64;
+    return GV_THREADS / lpr > base ? GV_THREADS / lpr : base;
+}
+
 // ---------------------------------------------------------------------------
-// down (and plain matvec): block = (64 output rows, one active expert).
+// down (and plain matvec): block = (down_rows_per_block output rows, one
+// active expert).
 // Routed mode adds w * y into out[token] with f32 atomics (out was cleared by
 // the preparation kernel); direct mode stores y to out[pos].
 // ---------------------------------------------------------------------------
@@ -294,7 +303,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true, G32>()
                                                                float *__restrict__ out,
                                                                GemvRoute r) {
     constexpr int RS = GV_THREADS / LPR;
-    constexpr int NR = 64;
+    constexpr int NR = down_rows_per_block(GPL, LPR);
     constexpr int NSTEP = NR / RS;
     constexpr int U = batch_rows<GPL, NSTEP>();
 
@@ -428,7 +437,8 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
                             hipStream_t st) {
     const GemvShape s = choose_shape(down.cols / 64);
     const int tb = tokens_per_pass(s, r, false);
-    const dim3 grid((down.rows + 63) / 64, r.rec ? r.max_active : 1);
+    const int nr = down_rows_per_block(s.gpl, s.lpr);
+    const dim3 grid((down.rows + nr - 1) / nr, r.rec ? r.max_active : 1);
     const bool g32 = down.group == 32;
 #define X(G_, L_, T_)                                                                        \
     if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                            \

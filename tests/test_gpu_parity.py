@@ -117,7 +117,9 @@ def test_matvec_one_hot_bit_exact():
 
 
 @pytest.mark.parametrize("rows,cols,batch,seed", [(256, 1024, 1, 0), (100, 320, 3, 9),
-                                                  (64, 6144, 2, 10), (513, 1536, 1, 11)])
+                                                  (64, 6144, 2, 10), (513, 1536, 1, 11),
+                                                  (37, 12288, 2, 12), (70, 8256, 1, 13),
+                                                  (45, 4160, 3, 14)])
 def test_matvec_random(rows, cols, batch, seed):
     say(f"matvec {rows}x{cols} batch {batch}")
     q, s, x = _matvec_inputs(rows, cols, seed, batch)
