@@ -40,6 +40,14 @@ inline bool mfma_fits(int64_t H, int64_t F, int64_t x_rows, int64_t h_rows) {
 int64_t packed_bytes(int64_t rows, int64_t cols) { return rows * ((cols + 1) / 2); }
 int64_t scale_count(int64_t rows, int64_t cols, int64_t g) { return rows * ((cols + g - 1) / g); }
 
+// The decode kernels read one matrix (one expert) through buffer descriptors
+// whose lanes past a row's end use an offset of 2^31: codes and scales of a
+// matrix must stay below 2 GB.
+inline bool gemv_fits(int64_t rows, int64_t cols, int64_t g) {
+    const int64_t lim = (int64_t)1 << 31;
+    return packed_bytes(rows, cols) < lim && 4 * scale_count(rows, cols, g) < lim;
+}
+
 // Group sizes the GPU kernels take for a row of `cols` inputs: 32, 64 times a
 // power of two (64, 128, 256, ...), or at least the row (one scale per row).
 bool group_supported(int group, int cols) {
@@ -57,6 +65,7 @@ int check_qmat(const qmoe_qmat *m, int rows, int cols, int experts) {
     if (m->rows != rows || m->cols != cols || rows <= 0 || cols <= 0) return QMOE_ERR_SHAPE;
     if (m->group <= 0) return QMOE_ERR_SHAPE;
     if (!group_supported(m->group, cols) || cols % 64 != 0) return QMOE_ERR_UNSUPPORTED;
+    if (!gemv_fits(rows, cols, m->group)) return QMOE_ERR_UNSUPPORTED;
     if (!m->q || !m->s) return QMOE_ERR_NULL;
     if (!aligned16(m->q) || !aligned16(m->s)) return QMOE_ERR_ALIGN;
     if (experts > 1) {
@@ -181,7 +190,7 @@ const char *qmoe_status_str(int status) {
         case QMOE_ERR_NULL: return "null pointer";
         case QMOE_ERR_SHAPE: return "bad shape or size";
         case QMOE_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
-        case QMOE_ERR_UNSUPPORTED: return "unsupported by the GPU kernels (group 32, 64 * 2^j or a whole row; cols % 64 == 0)";
+        case QMOE_ERR_UNSUPPORTED: return "unsupported by the GPU kernels (group 32, 64 * 2^j or a whole row; layer and FFN widths % 64 == 0; a matrix under 2 GB)";
         case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
         case QMOE_ERR_ALIAS: return "output overlaps an input or the workspace";
         case QMOE_ERR_ABI: return "struct_size mismatch (library and caller built from different headers)";
@@ -263,7 +272,8 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     if (batch < 0 || W->rows <= 0 || W->cols <= 0 || W->group <= 0) return QMOE_ERR_SHAPE;
     if (!group_supported(W->group, W->cols)) return QMOE_ERR_UNSUPPORTED;
     const MatvecPlan p = matvec_plan(W);
-    if (!gemv_supported((int)p.cols)) return QMOE_ERR_UNSUPPORTED;
+    if (!gemv_supported((int)p.cols) || !gemv_fits(W->rows, p.cols, p.group))
+        return QMOE_ERR_UNSUPPORTED;
     if (!W->q || !W->s) return QMOE_ERR_NULL;
     if (!aligned16(W->q) || !aligned16(W->s)) return QMOE_ERR_ALIGN;
     if (batch == 0) return QMOE_OK;

@@ -141,6 +141,8 @@ def test_matvec_and_pack_rejections(lib):
                            ws, nbp, None) == 4
     assert lib.qmoe_matvec(ctypes.byref(qmat(4, 20000)), FAKE, 1, FAKE + (30 << 32), ws,
                            1 << 30, None) == 4                            # wider than any shape
+    assert lib.qmoe_matvec(ctypes.byref(qmat(1 << 20, 4096)), FAKE, 1, FAKE + (30 << 32), ws,
+                           1 << 40, None) == 4                            # 2 GB of codes
     assert lib.qmoe_matvec(ctypes.byref(qmat(256, 1024, size=3)), FAKE, 1, FAKE, ws, nb,
                            None) == 7
     assert lib.qmoe_matvec(ctypes.byref(W), None, 1, FAKE + (30 << 32), ws, nb, None) == 1
