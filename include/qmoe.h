@@ -69,7 +69,10 @@ enum {
 };
 
 /* Activation dtypes.  The dtype of x selects the path: f32 = decode (GEMV
- * kernels), bf16 = prefill (grouped MFMA kernels). */
+ * kernels), bf16 = prefill (grouped MFMA kernels).  The bf16 path feeds the
+ * matrix cores f16 operands: q * s and the gated intermediate h must stay in
+ * the f16 range (|s| < 8188, |h| < 65504), larger values giving inf; the
+ * accumulators and every output are f32. */
 enum { QMOE_F32 = 0, QMOE_BF16 = 1 };
 
 /* One grouped int4 matrix, or a stack of per-expert matrices of one shape.
