@@ -409,8 +409,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path is single-GPU; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+              f"(the kernels and this benchmark run on a single GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch
