@@ -49,6 +49,38 @@ __device__ __forceinline__ uint32_t group_or(uint32_t v) {
     return v;
 }
 
+// DPP lane permutations inside a row of 16 lanes (every source lane lies in
+// the same row, so all of them are valid whenever the row is active).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+constexpr int DPP_QUAD_SWAP1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_SWAP2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
+// OR over each group of 8 lanes, in every lane of the group: quad pairs,
+// quads, then the two quads of a half row (half mirror maps one onto the
+// other).
+__device__ __forceinline__ uint32_t or8_dpp(uint32_t v) {
+    v |= dpp_u32<DPP_QUAD_SWAP1>(v);
+    v |= dpp_u32<DPP_QUAD_SWAP2>(v);
+    v |= dpp_u32<DPP_ROW_HALF_MIRROR>(v);
+    return v;
+}
+
+// Max over each group of 32 lanes, in every lane: within 16 lanes by DPP
+// (quad pairs, quads, half rows, rows), then one exchange between the two
+// rows.
+__device__ __forceinline__ float max32_dpp(float v) {
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v))));
+    return fmaxf(v, __shfl_xor(v, 16, QMOE_WAVE));
+}
+
 // Signed int4 x int4 dot of 8 nibbles, accumulated into c (v_dot8_i32_i4).
 __device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
     return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
@@ -83,7 +115,7 @@ constexpr int XD_FRAC_BITS = 18;
 // `store(plane, dword, value)` from lanes with (lane % 8) == 0.
 template <typename Store>
 __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
-    const float m = group_max<32>(fabsf(x));
+    const float m = max32_dpp(fabsf(x));
     float factor;
     int v = 0;
     if (!(m <= 3.0e38f)) {                    // inf or nan in the chunk
@@ -103,7 +135,7 @@ __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
         const int d = ((v + 8) & 15) - 8;
         v = (v - d) >> 4;
         uint32_t nib = (uint32_t)(d & 15) << (4 * sub);
-        nib = group_or<8>(nib);
+        nib = or8_dpp(nib);
         if (sub == 0) store(k, dw, nib);
     }
     return factor;

@@ -244,30 +244,35 @@ hipError_t launch_xdigits(const float *x, int rows, int cols, int src_cols, XDig
 
 // Inclusive scan over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < QMOE_WAVE; o <<= 1) {
-        const int y = __shfl_up(x, o, QMOE_WAVE);
-        if (lane >= o) x += y;
-    }
+    // Hillis-Steele inside each row of 16 lanes (row shifts read 0 past the
+    // row start), then the row totals carried forward with row broadcasts:
+    // lane 15 into rows 1 and 3, lane 31 into rows 2 and 3.  DPP only, no LDS.
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
     return x;
 }
 
 // The same worklist built by one wave, for small pair counts: no block
-// barriers, only the in-order LDS traffic of a single wave.
+// barriers, only the in-order LDS traffic of a single wave (its fences are
+// wave-scope: they order the compiler, the hardware already keeps one
+// wave's LDS operations in order).
 __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int n,
                         int k, int E, const Worklist &wl, const DecodePlan &plan,
                         int *cnt /* [E+1] */, int *run /* [E+1] */) {
     const int lane = lane_id();
     for (int e = lane; e <= E; e += QMOE_WAVE) cnt[e] = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     for (int p = lane; p < n; p += QMOE_WAVE) {
         int e = ids[p];
         if (e < 0 || e >= E) e = E;
         atomicAdd(&cnt[e], 1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     int carry = 0, acarry = 0;
     for (int base = 0; base < E; base += QMOE_WAVE) {
@@ -290,8 +295,8 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
                 rc[3] = 0;
             }
         }
-        carry += __shfl(inc, QMOE_WAVE - 1, QMOE_WAVE);
-        acarry += __shfl(ainc, QMOE_WAVE - 1, QMOE_WAVE);
+        carry += __builtin_amdgcn_readlane(inc, QMOE_WAVE - 1);
+        acarry += __builtin_amdgcn_readlane(ainc, QMOE_WAVE - 1);
     }
     if (lane == 0) {
         wl.offsets[E] = carry;
@@ -301,7 +306,7 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
     }
     if (plan.rec)
         for (int a = acarry + lane; a < plan.max_active; a += QMOE_WAVE) plan.rec[4 * a] = -1;
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     int nbits = 1;
     while ((1 << nbits) <= E) nbits++;
@@ -331,10 +336,10 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
                 plan.wsort[pos] = topk_w[p];
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
         if (act && rank == 0) run[e] += cnt_e;
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
 }
