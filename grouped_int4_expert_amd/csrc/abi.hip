@@ -108,7 +108,8 @@ struct LayerWs {
     XDigits xd, hd;
     DecodePlan plan;
     uint16_t *x16, *h16;
-    float *xinv, *y;
+    float *xinv;
+    YBuf y;
     int64_t bytes;
     int max_active, max_tiles;
     qmoe_layer_ws_view view;
@@ -144,7 +145,8 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
         L.x16 = c.take<uint16_t>((int64_t)T * H);
         L.xinv = c.take<float>(T);
         L.h16 = c.take<uint16_t>(n * F);
-        L.y = c.take<float>(n * H);
+        L.y.v = c.take<uint16_t>(n * H);
+        L.y.e = c.take<int8_t>(n * (H / 16));
     }
     L.bytes = c.off;
     // offsets of the worklist arrays (same order as above)
@@ -387,7 +389,7 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
         e = launch_xprep(static_cast<const uint16_t *>(x), batch, H, x16, xinv, st);
         if (e == hipSuccess)
             e = launch_mfma_gateup(to_qmat(gate), to_qmat(up), x16, xinv, h16, r, st);
-        if (e == hipSuccess) e = launch_mfma_down(to_qmat(down), h16, out, r, st);
+        if (e == hipSuccess) e = launch_mfma_down(to_qmat(down), h16, out, YBuf{}, r, st);
     }
     return status_of(e);
 }
@@ -585,7 +587,7 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         r.h_rows = n;
         if (e == hipSuccess) e = launch_mfma_gateup(G, U, L.x16, L.xinv, L.h16, r, st);
         if (e == hipSuccess) e = mark();
-        if (e == hipSuccess) e = launch_mfma_down(D, L.h16, L.y, r, st);
+        if (e == hipSuccess) e = launch_mfma_down(D, L.h16, nullptr, L.y, r, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_combine(L.y, L.wl.inv, tokens, k, H, out, st);
         if (e == hipSuccess) e = mark();

@@ -15,6 +15,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef _Float16 __attribute__((ext_vector_type(2))) f16x2;
+typedef _Float16 __attribute__((ext_vector_type(4))) f16x4;
 
 // Lanes per wave and the lane index.
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (QMOE_WAVE - 1); }
@@ -70,14 +71,19 @@ __device__ __forceinline__ uint32_t or8_dpp(uint32_t v) {
     return v;
 }
 
+// Max over each row of 16 lanes, in every lane of the row (DPP only).
+__device__ __forceinline__ float max16_dpp(float v) {
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v))));
+    return fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v))));
+}
+
 // Max over each group of 32 lanes, in every lane: within 16 lanes by DPP
 // (quad pairs, quads, half rows, rows), then one exchange between the two
 // rows.
 __device__ __forceinline__ float max32_dpp(float v) {
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP1>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QUAD_SWAP2>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v))));
+    v = max16_dpp(v);
     return fmaxf(v, __shfl_xor(v, 16, QMOE_WAVE));
 }
 

@@ -133,12 +133,19 @@ hipError_t launch_xprep(const uint16_t *x, int tokens, int hidden, uint16_t *x16
 hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *x16,
                               const float *xinv, uint16_t *h16, const MfmaRoute &r,
                               hipStream_t st);
-// Y[pos][H] = w * (D h) in f32 (direct mode: out[t] = D h).
-hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y,
+// Y of the routed prefill down projection: Y[pos][n] = v[pos][n] * 2^(e - 15)
+// with v f16 and e an int8 exponent shared by each 4-row x 16-column block
+// (stored once per row: e[pos][n / 16]); |v| < 2^15 by construction.
+struct YBuf {
+    uint16_t *v;   // [pairs][hidden] f16
+    int8_t *e;     // [pairs][hidden / 16]
+};
+// Routed: Y[pos] = w * (D h) into y; direct mode: out[t] = D h in f32.
+hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *out, YBuf y,
                             const MfmaRoute &r, hipStream_t st);
-// out[t] = sum_j Y[inv[t*k + j]] (dropped pairs skipped).
-hipError_t launch_combine(const float *y, const int32_t *inv, int tokens, int k, int hidden,
-                          float *out, hipStream_t st);
+// out[t] = sum_j Y[inv[t*k + j]] in pick order (dropped pairs skipped).
+hipError_t launch_combine(YBuf y, const int32_t *inv, int tokens, int k, int hidden, float *out,
+                          hipStream_t st);
 
 // Router: ids [tokens][k] (pick order) and softmax weights over the picked
 // logits, one wave per token.

@@ -151,16 +151,21 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_gateup_kernel(
     }
 }
 
-__global__ void __launch_bounds__(256) combine_kernel(const float *__restrict__ y,
-                                                      const int32_t *__restrict__ inv, int k,
-                                                      int hidden, float *__restrict__ out) {
+// out[t][n..n+3] = sum over j in pick order of Y[inv[t k + j]][n..n+3]; the
+// four columns share one exponent (n % 4 == 0 stays inside a 16-column block).
+__global__ void __launch_bounds__(256) combine_kernel(YBuf y, const int32_t *__restrict__ inv,
+                                                      int k, int hidden, float *__restrict__ out) {
     const int t = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (n >= hidden) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; j++) {
         const int pos = inv[(int64_t)t * k + j];
-        if (pos >= 0) acc += *(const f32x4 *)(y + (int64_t)pos * hidden + n);
+        if (pos >= 0) {
+            const f16x4 v = *(const f16x4 *)(y.v + (int64_t)pos * hidden + n);
+            const float sc = ldexpf(1.0f, (int)y.e[(int64_t)pos * (hidden / 16) + n / 16] - 15);
+            acc += f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]} * sc;
+        }
     }
     *(f32x4 *)(out + (int64_t)t * hidden + n) = acc;
 }
@@ -186,8 +191,8 @@ hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *y, const int32_t *inv, int tokens, int k, int hidden,
-                          float *out, hipStream_t st) {
+hipError_t launch_combine(YBuf y, const int32_t *inv, int tokens, int k, int hidden, float *out,
+                          hipStream_t st) {
     const dim3 grid((hidden / 4 + 255) / 256, tokens);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, y, inv, k, hidden, out);
     return hipGetLastError();

@@ -10,7 +10,7 @@ namespace qmoe {
 // ---------------------------------------------------------------------------
 template <int BMK, bool G32>
 __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
-    QMat D, const uint16_t *__restrict__ h16, float *__restrict__ y, MfmaRoute r) {
+    QMat D, const uint16_t *__restrict__ h16, float *__restrict__ out, YBuf yb, MfmaRoute r) {
     constexpr int MF = mf_of<BMK>();
     __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
         s2[BMK * 64], s3[BMK * 64];
@@ -48,34 +48,72 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
     Frags<MF> fr;
     run_mainloop<MF, G32>(fr, src, ng, ti.rows, s0, s1, s2, s3);
 
+    if (!routed) {   // direct mode (one expert): out = D h in f32
+#pragma unroll
+        for (int i = 0; i < MF; i++) {
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int m = acc_row(i, v, lane);
+                if (m < ti.rows) {
+#pragma unroll
+                    for (int j = 0; j < NF; j++)
+                        if (ncol[j] < H) out[(int64_t)(ti.pos0 + m) * H + ncol[j]] = fr.acc[i][j][v];
+                }
+            }
+        }
+        return;
+    }
+    // Routed: Y = w (D h) as f16 with a power-of-two exponent per block of 4
+    // rows (the lane's accumulators 4g..4g+3) x 16 columns (one DPP row of
+    // lanes): the block maximum is scaled into [2^14, 2^15), so every value
+    // keeps f16's 11-bit significand and none overflows.  Lane r (< 4) of each
+    // 16-lane row stores the exponent of row r of the block.
+    const int hs = H / 16;
 #pragma unroll
     for (int i = 0; i < MF; i++) {
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            const int m = acc_row(i, v, lane);
-            if (m < ti.rows) {
-                const int pos = ti.pos0 + m;
-                const float wgt = sW[m];
+        for (int j = 0; j < NF; j++) {
 #pragma unroll
-                for (int j = 0; j < NF; j++)
-                    if (ncol[j] < H) y[(int64_t)pos * H + ncol[j]] = wgt * fr.acc[i][j][v];
+            for (int g = 0; g < 4; g++) {
+                const int rbase = 32 * i + 8 * g + 4 * hh;
+                float val[4], mx = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 4; rr++) {
+                    val[rr] = sW[rbase + rr] * fr.acc[i][j][4 * g + rr];
+                    mx = fmaxf(mx, fabsf(val[rr]));
+                }
+                mx = max16_dpp(mx);
+                int ex = 0;
+                if (mx > 0.f && mx <= 3.4e38f) frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
+                ex = max(ex, -126);
+                const float sc = ldexpf(1.0f, 15 - ex);
+                if (ncol[j] < H) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; rr++)
+                        if (rbase + rr < ti.rows)
+                            yb.v[(int64_t)(ti.pos0 + rbase + rr) * H + ncol[j]] =
+                                __builtin_bit_cast(uint16_t, (_Float16)(val[rr] * sc));
+                    const int rr = lane & 15;
+                    if (rr < 4 && rbase + rr < ti.rows)
+                        yb.e[(int64_t)(ti.pos0 + rbase + rr) * hs + ((ncol[j] - rr) >> 4)] = (int8_t)ex;
+                }
             }
         }
     }
 }
 
 // out[t] = sum_j Y[inv[t*k + j]], slots in order; 4 floats per thread.
-hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *y, const MfmaRoute &r,
-                            hipStream_t st) {
+hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *out, YBuf y,
+                            const MfmaRoute &r, hipStream_t st) {
     constexpr int BMK = DOWN_BM;
     const int64_t items = r.wl.pairs ? (int64_t)r.max_tiles * (BM / BMK) : (r.ntok + BMK - 1) / BMK;
     const dim3 grid(xcd_grid(items * ((down.rows + 255) / 256)));
     if (down.group == 32)
         hipLaunchKernelGGL((mfma_down_kernel<BMK, true>), grid, dim3(MF_THREADS), 0, st, down, h16,
-                           y, r);
+                           out, y, r);
     else
         hipLaunchKernelGGL((mfma_down_kernel<BMK, false>), grid, dim3(MF_THREADS), 0, st, down,
-                           h16, y, r);
+                           h16, out, y, r);
     return hipGetLastError();
 }
 

@@ -336,6 +336,23 @@ def test_layer_other_aspect_ratios(H, F, dtype):
     assert err <= (F32_TOL if dtype == "f32" else BF16_TOL)
 
 
+def test_layer_bf16_outputs_beyond_f16_range():
+    """Per-pair down outputs beyond 65504 (down scales x30000, so |q s| stays
+    below 4800 while outputs reach ~1e5): the f16 intermediate of the routed
+    down projection carries a power-of-two exponent per 4 x 16 block, so
+    nothing overflows."""
+    say("layer bf16 with outputs beyond the f16 range")
+    L = Layer(8, 512, 256, seed=41)
+    L.s["sd"] = L.s["sd"] * 30000.0
+    L.s_dev["sd"].mul_(30000.0)
+    out, ref = _layer_case(L, 50, 2, "bf16", seed=42)
+    assert np.abs(ref).max() > 1e5
+    assert np.isfinite(out).all()
+    err = rel_l2(out, ref)
+    say(f"  max |ref| = {np.abs(ref).max():.3e}, rel_l2 = {err:.3e}")
+    assert err <= BF16_TOL
+
+
 def test_layer_wide_topk():
     """k = 16 of 32 experts, f32 and bf16."""
     L = Layer(32, 256, 128, seed=33)
