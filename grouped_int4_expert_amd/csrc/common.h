@@ -99,6 +99,14 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// The same with the hardware exp2 and reciprocal (about 1 ulp each), for
+// results that are rounded to f16 next: z * 1/(1 + 2^(-z log2 e)).  Large
+// negative z gives 2^t = inf, 1/inf = 0 and a zero of z's sign, as above.
+__device__ __forceinline__ float silu_fast(float z) {
+    const float e = __builtin_amdgcn_exp2f(z * -1.4426950408889634f);
+    return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // ---------------------------------------------------------------------------
 // Activation digits ("x digits").  A 32-element chunk of an f32 activation
 // row is carried as a block fixed-point integer v_i = rint(x_i * 2^(18-E))

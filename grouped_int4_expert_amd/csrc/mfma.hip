@@ -99,7 +99,7 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_gateup_kernel(
     constexpr int MF = mf_of<BMK>();
     __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
         s2[BMK * 64], s3[BMK * 64];
-    __shared__ float sInv[BMK];
+    __shared__ __attribute__((aligned(16))) float sInv[BMK];
 
     const int H = G.cols, F = G.rows, ng = H / 64;
     int tile, cb;
@@ -135,17 +135,25 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_gateup_kernel(
     run_mainloop<MF, G32>(fr, src, ng, ti.rows, s0, s1, s2, s3);
 
     if (!wave_on) return;
+    // h rows of the tile through a descriptor that ends at row ti.rows:
+    // stores of rows past the tile fall outside it and are dropped, so the
+    // loop has no branches; the row offset rides in the vector offset.
     const int npos = (n & ~7) + octet_pos(n & 7);
+    const __amdgpu_buffer_rsrc_t hr =
+        make_rsrc(h16 + (int64_t)ti.pos0 * F, (int64_t)ti.rows * F * 2);
+    const uint32_t hoff = (uint32_t)((4 * hh * F + npos) * 2);
 #pragma unroll
     for (int i = 0; i < MF; i++) {
 #pragma unroll
-        for (int v = 0; v < 16; v++) {
-            const int m = acc_row(i, v, lane);
-            if (m < ti.rows) {
-                const float sc = sInv[m];
-                const float h = silu(fr.acc[i][0][v] * sc) * (fr.acc[i][1][v] * sc);
-                h16[(int64_t)(ti.pos0 + m) * F + npos] =
-                    __builtin_bit_cast(uint16_t, (_Float16)h);
+        for (int q = 0; q < 4; q++) {
+            const f32x4 sc4 = *(const f32x4 *)&sInv[32 * i + 8 * q + 4 * hh];
+#pragma unroll
+            for (int rr = 0; rr < 4; rr++) {
+                const int v = 4 * q + rr;   // row 32 i + 8 q + 4 hh + rr
+                const float h = silu_fast(fr.acc[i][0][v] * sc4[rr]) * (fr.acc[i][1][v] * sc4[rr]);
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    __builtin_bit_cast(uint16_t, (_Float16)h), hr,
+                    hoff + (uint32_t)((32 * i + 8 * q + rr) * F * 2), 0, 0);
             }
         }
     }
