@@ -561,7 +561,7 @@ def main():
     dec_roof = roof_step - p_roof
     achieved = p_gu_flops / (gateup_ms * 1e-3)
     kernel_src = [os.path.join(ROOT, "grouped_int4_expert_amd", "csrc", f)
-                  for f in ("mfma.hip", "mfma_loop.h")]
+                  for f in ("mfma_gateup.h", "mfma_loop.h", "mfma.hip")]
     rec = {
         "metric": "int4-g64 MoE expert GB/s (decode) + TFLOP/s (8K prefill), % of roofline",
         "value": round(value, 3),

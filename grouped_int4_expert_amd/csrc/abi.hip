@@ -31,10 +31,14 @@ inline bool overlap(const void *a, int64_t na, const void *b, int64_t nb) {
 inline int status_of(hipError_t e) { return e == hipSuccess ? QMOE_OK : QMOE_ERR_HIP; }
 
 // The prefill kernels address activations, h and each expert's weights
-// through buffer descriptors with 32-bit byte sizes and offsets.
+// through buffer descriptors with 32-bit byte sizes and offsets; the
+// epilogues store a tile's rows (at most 256) through one descriptor, with
+// 2^31 added to the offset of a lane that must not store, so a tile's h and Y
+// rows must span less than 2^31 bytes.
 inline bool mfma_fits(int64_t H, int64_t F, int64_t x_rows, int64_t h_rows) {
     const int64_t lim = (int64_t)1 << 32;
-    return x_rows * H * 2 < lim && h_rows * F * 2 < lim && H * F / 2 < lim && H * F / 8 < lim;
+    return x_rows * H * 2 < lim && h_rows * F * 2 < lim && H * F / 2 < lim && H * F / 8 < lim &&
+           256 * 2 * (H > F ? H : F) < lim / 2;
 }
 
 int64_t packed_bytes(int64_t rows, int64_t cols) { return rows * ((cols + 1) / 2); }

@@ -14,7 +14,7 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
     constexpr int MF = mf_of<BMK>();
     __shared__ __attribute__((aligned(1024))) uint16_t s0[BMK * 64], s1[BMK * 64],
         s2[BMK * 64], s3[BMK * 64];
-    __shared__ float sW[BMK];
+    __shared__ __attribute__((aligned(16))) float sW[BMK];
 
     const int H = D.rows, F = D.cols, ng = F / 64;
     int tile, cb;
@@ -68,18 +68,32 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
     // lanes): the block maximum is scaled into [2^14, 2^15), so every value
     // keeps f16's 11-bit significand and none overflows.  Lane r (< 4) of each
     // 16-lane row stores the exponent of row r of the block.
+    // Stores go through descriptors that end at row ti.rows (rows past the
+    // tile are dropped); columns past H and the exponent stores of lanes
+    // 4..15 of each DPP row take an offset past any descriptor.
     const int hs = H / 16;
+    const __amdgpu_buffer_rsrc_t yv = make_rsrc(yb.v + (int64_t)ti.pos0 * H, (int64_t)ti.rows * H * 2);
+    const __amdgpu_buffer_rsrc_t ye = make_rsrc(yb.e + (int64_t)ti.pos0 * hs, (int64_t)ti.rows * hs);
+    const int er = lane & 15;   // row of the block whose exponent this lane stores
+    uint32_t voff[NF], eoff[NF];
+#pragma unroll
+    for (int j = 0; j < NF; j++) {
+        const bool on = ncol[j] < H;
+        voff[j] = on ? (uint32_t)((4 * hh * H + ncol[j]) * 2) : OOB_OFFSET;
+        eoff[j] = on && er < 4 ? (uint32_t)((4 * hh + er) * hs + ((ncol[j] - er) >> 4)) : OOB_OFFSET;
+    }
 #pragma unroll
     for (int i = 0; i < MF; i++) {
 #pragma unroll
-        for (int j = 0; j < NF; j++) {
+        for (int g = 0; g < 4; g++) {
+            const int rb = 32 * i + 8 * g;   // rows rb + 4 hh .. + 3
+            const f32x4 w4 = *(const f32x4 *)&sW[rb + 4 * hh];
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int rbase = 32 * i + 8 * g + 4 * hh;
+            for (int j = 0; j < NF; j++) {
                 float val[4], mx = 0.f;
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++) {
-                    val[rr] = sW[rbase + rr] * fr.acc[i][j][4 * g + rr];
+                    val[rr] = w4[rr] * fr.acc[i][j][4 * g + rr];
                     mx = fmaxf(mx, fabsf(val[rr]));
                 }
                 mx = max16_dpp(mx);
@@ -87,16 +101,13 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
                 if (mx > 0.f && mx <= 3.4e38f) frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
                 ex = max(ex, -126);
                 const float sc = ldexpf(1.0f, 15 - ex);
-                if (ncol[j] < H) {
 #pragma unroll
-                    for (int rr = 0; rr < 4; rr++)
-                        if (rbase + rr < ti.rows)
-                            yb.v[(int64_t)(ti.pos0 + rbase + rr) * H + ncol[j]] =
-                                __builtin_bit_cast(uint16_t, (_Float16)(val[rr] * sc));
-                    const int rr = lane & 15;
-                    if (rr < 4 && rbase + rr < ti.rows)
-                        yb.e[(int64_t)(ti.pos0 + rbase + rr) * hs + ((ncol[j] - rr) >> 4)] = (int8_t)ex;
-                }
+                for (int rr = 0; rr < 4; rr++)
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        __builtin_bit_cast(uint16_t, (_Float16)(val[rr] * sc)), yv,
+                        voff[j] + (uint32_t)((rb + rr) * H * 2), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(int8_t)ex, ye,
+                                                     eoff[j] + (uint32_t)(rb * hs), 0, 0);
             }
         }
     }

@@ -280,17 +280,20 @@ __device__ __forceinline__ int acc_row(int i, int v, int lane) {
     return 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 }
 
-// Runs the main loop over the row fragments a tile of `rows` rows needs
-// (rounded up to MF, MF/2 or MF/4 fragments).
-template <int MF, bool G32>
+// Runs the main loop over the row fragments a tile of `rows` rows needs:
+// ceil(rows / 32) of them, so a tile's padding is under one fragment.
+template <int MF, bool G32, int C = MF>
 __device__ __forceinline__ void run_mainloop(Frags<MF> &fr, const LoopSrc<MF> &src, int ng, int rows,
                                              uint16_t *__restrict__ s0,
                                              uint16_t *__restrict__ s1,
                                              uint16_t *__restrict__ s2,
                                              uint16_t *__restrict__ s3) {
-    if (rows > 16 * MF) mfma_mainloop<MF, MF, G32>(fr, src, ng, s0, s1, s2, s3);
-    else if (rows > 8 * MF) mfma_mainloop<MF, MF / 2, G32>(fr, src, ng, s0, s1, s2, s3);
-    else mfma_mainloop<MF, MF / 4, G32>(fr, src, ng, s0, s1, s2, s3);
+    if constexpr (C == 1) {
+        mfma_mainloop<MF, 1, G32>(fr, src, ng, s0, s1, s2, s3);
+    } else {
+        if (rows > 32 * (C - 1)) mfma_mainloop<MF, C, G32>(fr, src, ng, s0, s1, s2, s3);
+        else run_mainloop<MF, G32, C - 1>(fr, src, ng, rows, s0, s1, s2, s3);
+    }
 }
 
 // Activation tile sources: load i of wave w fills rows 32i + 8w + lane/8,

@@ -189,6 +189,26 @@ def test_layer_bf16_multi_tile(T, k):
     assert err <= BF16_TOL
 
 
+def test_layer_bf16_every_fragment_count():
+    # Expert e gets exactly COUNTS[e] rows, so tiles end after each number of
+    # 32-row fragments (1 .. 8), on and beside fragment and tile borders;
+    # every expert's rows are checked on their own.
+    counts = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 129, 160, 161, 192, 193,
+              224, 225, 255, 256, 257, 300, 511, 513, 0]
+    E, T = len(counts), sum(counts)
+    say(f"layer bf16 E={E} H=256 F=128 T={T} k=1, fixed rows per expert")
+    L = Layer(E, 256, 128, seed=27)
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(27))
+    assign = torch.repeat_interleave(torch.arange(E), torch.tensor(counts))[perm]
+    out, ref = _layer_case(L, T, 1, "bf16", seed=27,
+                           mutate=lambda ids, w: (assign.view(T, 1).to(ids.dtype), w))
+    for e in range(E - 1):
+        rows = (assign == e).nonzero().flatten().numpy()
+        err = rel_l2(out[rows], ref[rows])
+        assert err <= BF16_TOL, (e, counts[e], err)
+    assert rel_l2(out, ref) <= BF16_TOL
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_invalid_and_duplicate_ids(dtype):
     say(f"layer invalid/duplicate ids {dtype}")
