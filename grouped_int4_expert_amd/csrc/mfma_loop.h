@@ -23,8 +23,16 @@ constexpr int occ_of() { return BMK > 128 ? 1 : 2; }   // blocks per CU
 constexpr int GATEUP_BM = 256;
 constexpr int DOWN_BM = 128;
 
-// LDS offset (in 16-bit elements) of octet `o` of row `m` in a BMK x 64 tile.
-__device__ __forceinline__ int sw_off(int m, int o) { return m * 64 + ((o ^ (m & 7)) << 3); }
+// Swizzle slot of octet `o` (16 bytes) in row `m` of a BMK x 64 f16 tile
+// (128-byte rows), and its LDS offset in 16-bit elements.  gfx950's LDS has
+// 64 four-byte banks and serves a 128-bit read 16 lanes at a time; an
+// operand read has those lanes on 16 consecutive rows at one octet.  XOR with
+// m % 8 spreads 8 rows over the 8 slots of a row, and XOR with bit 3 of m
+// separates rows m and m + 8, which sit on the same banks (row stride 128
+// bytes, bank line 256): the 16 reads then hit 16 distinct bank quads
+// (SQ_LDS_BANK_CONFLICT reads 0; with m % 8 alone, every read was 2-way).
+__device__ __forceinline__ int sw_slot(int m, int o) { return o ^ (m & 7) ^ ((m >> 3) & 1); }
+__device__ __forceinline__ int sw_off(int m, int o) { return m * 64 + (sw_slot(m, o) << 3); }
 
 // Position of element e (0..7) of an octet after the unpack permutation.
 __device__ __forceinline__ int octet_pos(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
@@ -296,17 +304,18 @@ __device__ __forceinline__ void run_mainloop(Frags<MF> &fr, const LoopSrc<MF> &s
     }
 }
 
-// Activation tile sources: load i of wave w fills rows 32i + 8w + lane/8,
-// whose swizzle slot lane%8 holds octet (lane%8) ^ (row%8).  Rows past the
+// Activation tile sources: load i of wave w fills rows m = 32i + 8w + lane/8,
+// and lane l fetches the octet that swizzle slot l % 8 of row m holds (the
+// swizzle is an involution on the slot: sw_slot(m, l % 8)).  Rows past the
 // tile read a valid row (row 0) and are never stored.
 template <int MF, typename RowOf>
 __device__ __forceinline__ void tile_offsets(LoopSrc<MF> &src, int rows, int row_elems,
                                              RowOf row_of) {
     const int lane = lane_id(), w = wave_id();
-    const int oct = (lane & 7) ^ ((lane >> 3) & 7);
 #pragma unroll
     for (int i = 0; i < MF; i++) {
         int m = 32 * i + 8 * w + (lane >> 3);
+        const int oct = sw_slot(m, lane & 7);
         if (m >= rows) m = 0;
         src.aoff[i] = (uint32_t)(row_of(m) * row_elems * 2 + oct * 16);
     }
