@@ -40,6 +40,11 @@
  *    16-byte aligned (QMOE_ERR_ALIGN otherwise), like the vector-load guard
  *    of the pxq_llama.cpp notes (release rc3 fixes) that declines rather
  *    than faults.
+ *  - Size limits (QMOE_ERR_SHAPE or QMOE_ERR_UNSUPPORTED beyond them): the
+ *    kernels address memory through buffer descriptors with 32-bit byte
+ *    offsets, so one expert matrix's codes and scales stay below 2 GB; on
+ *    the bf16 path the activations [tokens][hidden] and h [pairs][inter] as
+ *    f16 stay below 4 GB and hidden and inter below 2^22.
  *  - Bad expert ids (outside [0, E)) are data, not arguments: they are
  *    dropped (contribute zero) and counted into an int32 on the device.
  */

@@ -122,6 +122,10 @@ def test_layer_rejections(lib):
     d6 = layer_desc()
     d6.gate.s = None
     assert call_layer(lib, d6) == 1
+    # bf16 path: a tile's h and Y rows go through one descriptor each, so
+    # hidden and inter stay below 2^22
+    assert call_layer(lib, layer_desc(H=1 << 22, F=64), dtype=1) == 2
+    assert call_layer(lib, layer_desc(H=64, F=1 << 22), dtype=1) == 2
 
 
 def test_matvec_and_pack_rejections(lib):
