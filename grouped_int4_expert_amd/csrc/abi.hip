@@ -137,10 +137,11 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
     L.wl.tile_m = MFMA_BM;
     L.hist = c.take<int32_t>(wl_scratch_ints(n, E));
     if (dtype == QMOE_F32) {
-        L.plan.rec = c.take<int32_t>(4 * (int64_t)L.max_active);
+        L.plan.rec_gu = c.take<int32_t>(4 * n);
+        L.plan.rec_dn = c.take<int32_t>(4 * n);
         L.plan.tok = c.take<int32_t>(n);
         L.plan.wsort = c.take<float>(n);
-        L.plan.max_active = L.max_active;
+        L.plan.max_rec = (int)n;
         L.xd.dig = c.take<uint32_t>((int64_t)T * (H / 32) * 20);
         L.xd.fac = c.take<float>((int64_t)T * (H / 32));
         L.hd.dig = c.take<uint32_t>(n * (F / 32) * 20);
@@ -564,17 +565,21 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         Worklist wl = L.wl;
         wl.tiles = nullptr;
         wl.n_tiles = nullptr;
-        e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, L.plan,
+        DecodePlan plan = L.plan;
+        plan.tb_gu = gemv_tokens_per_pass(G, tokens, true);
+        plan.tb_dn = gemv_tokens_per_pass(D, tokens, false);
+        e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, plan,
                                static_cast<const float *>(x), tokens, H, L.xd, out, st);
         if (e == hipSuccess) e = mark();
         GemvRoute r{};
-        r.rec = L.plan.rec;
-        r.tok = L.plan.tok;
-        r.wsort = L.plan.wsort;
-        r.max_active = L.max_active;
+        r.rec = plan.rec_gu;
+        r.tok = plan.tok;
+        r.wsort = plan.wsort;
+        r.max_rec = plan.max_rec;
         r.batch_tokens = tokens;
         if (e == hipSuccess) e = launch_gemv_gateup(G, U, L.xd, L.hd, r, st);
         if (e == hipSuccess) e = mark();
+        r.rec = plan.rec_dn;
         if (e == hipSuccess) e = launch_gemv_down(D, L.hd, out, r, st);
         if (e == hipSuccess) e = mark();
     } else {

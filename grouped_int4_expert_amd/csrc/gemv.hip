@@ -162,7 +162,7 @@ __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XR
     return acc;
 }
 
-// Expert and sorted-position range of this block.
+// Expert and sorted-position range of this block (one plan record).
 __device__ __forceinline__ bool block_expert(const GemvRoute &r, int a, int &e, int &p0,
                                              int &p1) {
     if (r.rec == nullptr) {
@@ -407,16 +407,20 @@ bool gemv_supported(int cols) {
 // digits in registers once the batch has more than one token; the down
 // projection runs faster with one token per pass at every batch size (fewer
 // registers, more waves in flight; its extra passes hit in L2).
-static int tokens_per_pass(const GemvShape &s, const GemvRoute &r, bool gateup) {
+static int tokens_per_pass(const GemvShape &s, int batch_tokens, bool gateup) {
     if (s.gpl != 1 || !gateup) return 1;
-    return r.batch_tokens > 1 ? 2 : 1;
+    return batch_tokens > 1 ? 2 : 1;
+}
+
+int gemv_tokens_per_pass(const QMat &m, int batch_tokens, bool gateup) {
+    return tokens_per_pass(choose_shape(m.cols / 64), batch_tokens, gateup);
 }
 
 hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDigits hd,
                               const GemvRoute &r, hipStream_t st) {
     const GemvShape s = choose_shape(gate.cols / 64);
-    const int tb = tokens_per_pass(s, r, true);
-    const dim3 grid(gate.rows / 32, r.rec ? r.max_active : 1);
+    const int tb = tokens_per_pass(s, r.batch_tokens, true);
+    const dim3 grid(gate.rows / 32, r.rec ? r.max_rec : 1);
     const bool g32 = gate.group == 32;
 #define X(G_, L_, T_)                                                                          \
     if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                              \
@@ -436,9 +440,9 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
 hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const GemvRoute &r,
                             hipStream_t st) {
     const GemvShape s = choose_shape(down.cols / 64);
-    const int tb = tokens_per_pass(s, r, false);
+    const int tb = tokens_per_pass(s, r.batch_tokens, false);
     const int nr = down_rows_per_block(s.gpl, s.lpr);
-    const dim3 grid((down.rows + nr - 1) / nr, r.rec ? r.max_active : 1);
+    const dim3 grid((down.rows + nr - 1) / nr, r.rec ? r.max_rec : 1);
     const bool g32 = down.group == 32;
 #define X(G_, L_, T_)                                                                        \
     if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                            \

@@ -70,15 +70,20 @@ hipError_t launch_worklist(const int32_t *ids, int n, int k, int E, const Workli
                            int32_t *scratch, hipStream_t st);
 
 // Per-call plan of the decode GEMVs, written by the preparation kernel so a
-// GEMV block starts with one load: rec[4a..4a+3] = (expert, first and end
-// sorted position, 0) for active slot a (expert -1 past the last active
-// slot, up to max_active); tok/wsort = token and routing weight of each
-// sorted position.
+// GEMV block starts with one load.  One record per weight pass: an active
+// expert with c pairs gets ceil(c / tb) records of at most tb consecutive
+// sorted positions, (expert, first and end sorted position, 0), experts in
+// ascending order; records past the last are (-1, 0, 0, 0) up to max_rec.
+// The gate+up and down kernels take different tokens per pass, so each has
+// its own list.  tok/wsort = token and routing weight of each sorted
+// position.
 struct DecodePlan {
-    int32_t *rec;       // [4 * max_active]
+    int32_t *rec_gu;    // [4 * max_rec], passes of tb_gu pairs
+    int32_t *rec_dn;    // [4 * max_rec], passes of tb_dn pairs
     int32_t *tok;       // [n]
     float *wsort;       // [n]
-    int max_active;
+    int max_rec;        // >= the number of records of either list (n suffices)
+    int tb_gu, tb_dn;
 };
 
 // Decode preparation in one launch: the worklist and plan (block 0), x ->
@@ -97,10 +102,10 @@ hipError_t launch_xdigits(const float *x, int rows, int cols, int src_cols, XDig
 // offsets[e]..offsets[e+1]; in "direct" mode (wl.pairs == nullptr) there is
 // one expert (0) with positions 0..ntok-1 = tokens 0..ntok-1, weight 1.
 struct GemvRoute {
-    const int32_t *rec;    // plan records (nullptr: direct mode)
+    const int32_t *rec;    // plan records of this kernel (nullptr: direct mode)
     const int32_t *tok;    // token of each sorted position
     const float *wsort;    // routing weight of each sorted position
-    int max_active;        // grid bound on active experts
+    int max_rec;           // grid bound on records
     int ntok;              // direct mode: tokens
     int batch_tokens;      // tokens in the call (a launch-shape hint)
 };
@@ -112,6 +117,9 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
 hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const GemvRoute &r,
                             hipStream_t st);
 // y = W x for `batch` rows of digits.
+// Tokens per weight pass the decode kernels use for matrix `m` in a call of
+// `batch_tokens` tokens (the plan's pass length must match).
+int gemv_tokens_per_pass(const QMat &m, int batch_tokens, bool gateup);
 hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
                               hipStream_t st);
 

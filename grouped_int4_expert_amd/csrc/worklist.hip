@@ -274,7 +274,19 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    int carry = 0, acarry = 0;
+    // Plan records of expert e (c pairs from sorted position off): passes of
+    // tb pairs from record slot `slot` on.
+    auto records = [&](int32_t *rec, int tb, int slot, int e, int off, int c) {
+        for (int j = 0; j * tb < c; j++) {
+            int32_t *rc = rec + 4 * (slot + j);
+            rc[0] = e;
+            rc[1] = off + j * tb;
+            rc[2] = min(off + (j + 1) * tb, off + c);
+            rc[3] = 0;
+        }
+    };
+    const bool planned = plan.rec_gu != nullptr;
+    int carry = 0, acarry = 0, gcarry = 0, dcarry = 0;
     for (int base = 0; base < E; base += QMOE_WAVE) {
         const int e = base + lane;
         const int c = e < E ? cnt[e] : 0;
@@ -282,21 +294,23 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
         const int off = carry + inc - c;
         const int a = c > 0 ? 1 : 0;
         const int ainc = wave_inclusive_scan(a);
+        const int ng = planned ? (c + plan.tb_gu - 1) / plan.tb_gu : 0;
+        const int nd = planned ? (c + plan.tb_dn - 1) / plan.tb_dn : 0;
+        const int ginc = wave_inclusive_scan(ng), dinc = wave_inclusive_scan(nd);
         if (e < E) {
             wl.counts[e] = c;
             wl.offsets[e] = off;
             run[e] = off;
             if (a && wl.active) wl.active[acarry + ainc - 1] = e;
-            if (a && plan.rec) {
-                int32_t *rc = plan.rec + 4 * (acarry + ainc - 1);
-                rc[0] = e;
-                rc[1] = off;
-                rc[2] = off + c;
-                rc[3] = 0;
+            if (a && planned) {
+                records(plan.rec_gu, plan.tb_gu, gcarry + ginc - ng, e, off, c);
+                records(plan.rec_dn, plan.tb_dn, dcarry + dinc - nd, e, off, c);
             }
         }
         carry += __builtin_amdgcn_readlane(inc, QMOE_WAVE - 1);
         acarry += __builtin_amdgcn_readlane(ainc, QMOE_WAVE - 1);
+        gcarry += __builtin_amdgcn_readlane(ginc, QMOE_WAVE - 1);
+        dcarry += __builtin_amdgcn_readlane(dinc, QMOE_WAVE - 1);
     }
     if (lane == 0) {
         wl.offsets[E] = carry;
@@ -304,8 +318,10 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
         run[E] = carry;
         if (wl.n_active) wl.n_active[0] = acarry;
     }
-    if (plan.rec)
-        for (int a = acarry + lane; a < plan.max_active; a += QMOE_WAVE) plan.rec[4 * a] = -1;
+    if (planned) {
+        for (int a = gcarry + lane; a < plan.max_rec; a += QMOE_WAVE) plan.rec_gu[4 * a] = -1;
+        for (int a = dcarry + lane; a < plan.max_rec; a += QMOE_WAVE) plan.rec_dn[4 * a] = -1;
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     int nbits = 1;
