@@ -376,7 +376,8 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
         hd.fac = c.take<float>((int64_t)batch * (F / 32));
         GemvRoute r{};
         r.ntok = batch;
-        r.batch_tokens = batch;
+        r.pairs = batch;
+        r.experts = 1;
         e = launch_xdigits(static_cast<const float *>(x), batch, H, H, xd, st);
         if (e == hipSuccess) e = launch_gemv_gateup(to_qmat(gate), to_qmat(up), xd, hd, r, st);
         if (e == hipSuccess) e = launch_gemv_down(to_qmat(down), hd, out, r, st);
@@ -566,8 +567,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         wl.tiles = nullptr;
         wl.n_tiles = nullptr;
         DecodePlan plan = L.plan;
-        plan.tb_gu = gemv_tokens_per_pass(G, tokens, true);
-        plan.tb_dn = gemv_tokens_per_pass(D, tokens, false);
+        plan.tb_gu = gemv_tokens_per_pass(G, (int)n, E, true);
+        plan.tb_dn = gemv_tokens_per_pass(D, (int)n, E, false);
         e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, plan,
                                static_cast<const float *>(x), tokens, H, L.xd, out, st);
         if (e == hipSuccess) e = mark();
@@ -576,7 +577,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         r.tok = plan.tok;
         r.wsort = plan.wsort;
         r.max_rec = plan.max_rec;
-        r.batch_tokens = tokens;
+        r.pairs = (int)n;
+        r.experts = E;
         if (e == hipSuccess) e = launch_gemv_gateup(G, U, L.xd, L.hd, r, st);
         if (e == hipSuccess) e = mark();
         r.rec = plan.rec_dn;

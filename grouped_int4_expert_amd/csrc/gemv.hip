@@ -404,22 +404,25 @@ bool gemv_supported(int cols) {
             X(3, 8, 1)
 
 // Tokens per weight pass (measured on MI355X): gate+up keeps two tokens'
-// digits in registers once the batch has more than one token; the down
-// projection runs faster with one token per pass at every batch size (fewer
-// registers, more waves in flight; its extra passes hit in L2).
-static int tokens_per_pass(const GemvShape &s, int batch_tokens, bool gateup) {
+// digits in registers once there are at least half as many pairs as experts
+// (128 experts: 16 tokens x top-8 186.8 vs 189.4 us per call with one; at 4
+// tokens most experts have a single token, and the one-token instance, with
+// its higher occupancy, is faster: 69.4 vs 70.8 us); the down projection runs
+// faster with one token per pass at every batch size (fewer registers, more
+// waves in flight; its extra passes hit in L2).
+static int tokens_per_pass(const GemvShape &s, int pairs, int experts, bool gateup) {
     if (s.gpl != 1 || !gateup) return 1;
-    return batch_tokens > 1 ? 2 : 1;
+    return pairs > 1 && 2 * (int64_t)pairs >= experts ? 2 : 1;
 }
 
-int gemv_tokens_per_pass(const QMat &m, int batch_tokens, bool gateup) {
-    return tokens_per_pass(choose_shape(m.cols / 64), batch_tokens, gateup);
+int gemv_tokens_per_pass(const QMat &m, int pairs, int experts, bool gateup) {
+    return tokens_per_pass(choose_shape(m.cols / 64), pairs, experts, gateup);
 }
 
 hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDigits hd,
                               const GemvRoute &r, hipStream_t st) {
     const GemvShape s = choose_shape(gate.cols / 64);
-    const int tb = tokens_per_pass(s, r.batch_tokens, true);
+    const int tb = tokens_per_pass(s, r.pairs, r.experts, true);
     const dim3 grid(gate.rows / 32, r.rec ? r.max_rec : 1);
     const bool g32 = gate.group == 32;
 #define X(G_, L_, T_)                                                                          \
@@ -440,7 +443,7 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
 hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const GemvRoute &r,
                             hipStream_t st) {
     const GemvShape s = choose_shape(down.cols / 64);
-    const int tb = tokens_per_pass(s, r.batch_tokens, false);
+    const int tb = tokens_per_pass(s, r.pairs, r.experts, false);
     const int nr = down_rows_per_block(s.gpl, s.lpr);
     const dim3 grid((down.rows + nr - 1) / nr, r.rec ? r.max_rec : 1);
     const bool g32 = down.group == 32;
@@ -462,7 +465,8 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
 hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y, hipStream_t st) {
     GemvRoute r{};
     r.ntok = batch;
-    r.batch_tokens = batch;
+    r.pairs = batch;
+    r.experts = 1;
     return launch_gemv_down(w, xd, y, r, st);
 }
 

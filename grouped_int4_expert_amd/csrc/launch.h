@@ -107,7 +107,7 @@ struct GemvRoute {
     const float *wsort;    // routing weight of each sorted position
     int max_rec;           // grid bound on records
     int ntok;              // direct mode: tokens
-    int batch_tokens;      // tokens in the call (a launch-shape hint)
+    int pairs, experts;    // pairs and experts of the call (a launch-shape hint)
 };
 
 // h digits for the down projection: silu(gate x) * (up x) per sorted pair.
@@ -118,8 +118,9 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
                             hipStream_t st);
 // y = W x for `batch` rows of digits.
 // Tokens per weight pass the decode kernels use for matrix `m` in a call of
-// `batch_tokens` tokens (the plan's pass length must match).
-int gemv_tokens_per_pass(const QMat &m, int batch_tokens, bool gateup);
+// `pairs` (token, expert) pairs over `experts` experts (the plan's pass
+// length must match).
+int gemv_tokens_per_pass(const QMat &m, int pairs, int experts, bool gateup);
 hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
                               hipStream_t st);
 
