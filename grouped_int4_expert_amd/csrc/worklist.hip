@@ -277,13 +277,10 @@ __device__ void wl_wave(const int32_t *__restrict__ ids, const float *__restrict
     // Plan records of expert e (c pairs from sorted position off): passes of
     // tb pairs from record slot `slot` on.
     auto records = [&](int32_t *rec, int tb, int slot, int e, int off, int c) {
-        for (int j = 0; j * tb < c; j++) {
-            int32_t *rc = rec + 4 * (slot + j);
-            rc[0] = e;
-            rc[1] = off + j * tb;
-            rc[2] = min(off + (j + 1) * tb, off + c);
-            rc[3] = 0;
-        }
+        for (int j = 0; j * tb < c; j++)
+            *(u32x4 *)(rec + 4 * (slot + j)) =
+                u32x4{(uint32_t)e, (uint32_t)(off + j * tb),
+                      (uint32_t)min(off + (j + 1) * tb, off + c), 0u};
     };
     const bool planned = plan.rec_gu != nullptr;
     int carry = 0, acarry = 0, gcarry = 0, dcarry = 0;

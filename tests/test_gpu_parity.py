@@ -209,6 +209,28 @@ def test_layer_bf16_every_fragment_count():
     assert rel_l2(out, ref) <= BF16_TOL
 
 
+@pytest.mark.parametrize("E", [16, 1024])
+def test_layer_f32_fixed_rows_per_expert(E):
+    # Decode plan: an expert with c pairs gets ceil(c / tb) weight-pass
+    # records; counts below make passes of one and two tokens end on and
+    # beside every split.  16 experts: two tokens per gate+up pass; 1024
+    # experts (fewer pairs than half the experts): one.
+    counts = [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 33, 0]
+    T = sum(counts)
+    say(f"layer f32 E={E} H=256 F=128 T={T} k=1, fixed rows per expert")
+    L = Layer(E, 256, 128, seed=28)
+    perm = torch.randperm(T, generator=torch.Generator().manual_seed(28))
+    assign = torch.repeat_interleave(torch.arange(len(counts)), torch.tensor(counts))[perm]
+    assign = (assign * (E // 16)).to(torch.int32)   # spread over the experts
+    out, ref = _layer_case(L, T, 1, "f32", seed=28,
+                           mutate=lambda ids, w: (assign.view(T, 1).to(ids.dtype), w))
+    for e in range(len(counts) - 1):
+        rows = (assign == e * (E // 16)).nonzero().flatten().numpy()
+        err = rel_l2(out[rows], ref[rows])
+        assert err <= F32_TOL, (e, counts[e], err)
+    assert rel_l2(out, ref) <= F32_TOL
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_invalid_and_duplicate_ids(dtype):
     say(f"layer invalid/duplicate ids {dtype}")
