@@ -18,8 +18,10 @@
 // complement) meets an activation dword in one v_dot8_i32_i4: 5 dot
 // instructions per 8 weights, integer-exact, instead of 16+ f32 ops.  The
 // chunk sum is rebuilt in int32 and scaled once per chunk and group.
-// Each block owns one expert (from the device worklist) and a slice of rows;
-// all tokens routed to that expert share the weight stream.
+// Each block owns a slice of rows of one expert and one weight pass over
+// them (a plan record from the device worklist): the pass's tokens (one or
+// two) share the weight stream, and an expert with more tokens gets one
+// block per pass.
 #include "common.h"
 #include "launch.h"
 
@@ -230,7 +232,7 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
 }
 
 // ---------------------------------------------------------------------------
-// gate+up: block = (32 rows of F, one active expert); 32 gate rows and the
+// gate+up: block = (32 rows of F, one pass of one expert); 32 gate rows and the
 // same 32 up rows (64 row tasks).  Writes h = silu(g)*u for the 32 rows as
 // one digit chunk per sorted position.
 // ---------------------------------------------------------------------------
@@ -294,7 +296,7 @@ __host__ __device__ constexpr int down_rows_per_block(int gpl, int lpr) {
 
 // ---------------------------------------------------------------------------
 // down (and plain matvec): block = (down_rows_per_block output rows, one
-// active expert).
+// pass of one expert).
 // Routed mode adds w * y into out[token] with f32 atomics (out was cleared by
 // the preparation kernel); direct mode stores y to out[pos].
 // ---------------------------------------------------------------------------
