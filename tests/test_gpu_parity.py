@@ -365,11 +365,13 @@ def test_layer_tiny_batches(dtype, T):
     assert rel_l2(out, ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
 
 
-@pytest.mark.parametrize("H,F", [(512, 1024), (1536, 512)])
+@pytest.mark.parametrize("H,F", [(512, 1024), (1536, 512), (320, 192), (192, 320)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_other_aspect_ratios(H, F, dtype):
     """Intermediate wider than hidden and the reverse, beside the 4096/1536
-    and 6144/2048 shapes."""
+    and 6144/2048 shapes; 320 and 192 leave the last 128-feature (gate+up)
+    and 256-feature (down) column blocks of the prefill kernels partly
+    empty and give the decode kernels rows of 3 or 5 groups."""
     say(f"layer E=8 H={H} F={F} T=33 k=2 {dtype}")
     L = Layer(8, H, F, seed=39)
     out, ref = _layer_case(L, 33, 2, dtype, seed=40)
