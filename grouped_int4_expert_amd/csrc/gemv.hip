@@ -164,6 +164,16 @@ __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XR
     return acc;
 }
 
+// Plan record of this block: grid y and z together (a grid dimension other
+// than x holds at most 65535 blocks; there can be one record per pair).
+__device__ __forceinline__ int record_index() { return blockIdx.z * gridDim.y + blockIdx.y; }
+
+inline dim3 gemv_grid(unsigned row_blocks, const GemvRoute &r) {
+    const int64_t nrec = r.rec ? r.max_rec : 1;
+    const int64_t gy = nrec < 65535 ? nrec : 65535;
+    return dim3(row_blocks, (unsigned)gy, (unsigned)((nrec + gy - 1) / gy));
+}
+
 // Expert and sorted-position range of this block (one plan record).
 __device__ __forceinline__ bool block_expert(const GemvRoute &r, int a, int &e, int &p0,
                                              int &p1) {
@@ -174,6 +184,7 @@ __device__ __forceinline__ bool block_expert(const GemvRoute &r, int a, int &e, 
         p1 = r.ntok;
         return true;
     }
+    if (a >= r.max_rec) return false;
     const u32x4 rc = *(const u32x4 *)(r.rec + 4 * a);
     e = (int)rc.x;
     if (e < 0) return false;
@@ -246,7 +257,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false, G32>(
     __shared__ float res[TB][NR];
 
     int e, p0, p1;
-    if (!block_expert(r, blockIdx.y, e, p0, p1)) return;
+    if (!block_expert(r, record_index(), e, p0, p1)) return;
     const int H = G.cols, F = G.rows;
     const int ng = H / 64, ncx = H / XD_CHUNK, nch = F / XD_CHUNK;
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
@@ -310,7 +321,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true, G32>()
     constexpr int U = batch_rows<GPL, NSTEP>();
 
     int e, p0, p1;
-    if (!block_expert(r, blockIdx.y, e, p0, p1)) return;
+    if (!block_expert(r, record_index(), e, p0, p1)) return;
     const int O = D.rows, I = D.cols;
     const int ng = I / 64, ncx = I / XD_CHUNK;
     const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
@@ -425,7 +436,7 @@ hipError_t launch_gemv_gateup(const QMat &gate, const QMat &up, XDigits xd, XDig
                               const GemvRoute &r, hipStream_t st) {
     const GemvShape s = choose_shape(gate.cols / 64);
     const int tb = tokens_per_pass(s, r.pairs, r.experts, true);
-    const dim3 grid(gate.rows / 32, r.rec ? r.max_rec : 1);
+    const dim3 grid = gemv_grid(gate.rows / 32, r);
     const bool g32 = gate.group == 32;
 #define X(G_, L_, T_)                                                                          \
     if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                              \
@@ -447,7 +458,7 @@ hipError_t launch_gemv_down(const QMat &down, XDigits hd, float *out, const Gemv
     const GemvShape s = choose_shape(down.cols / 64);
     const int tb = tokens_per_pass(s, r.pairs, r.experts, false);
     const int nr = down_rows_per_block(s.gpl, s.lpr);
-    const dim3 grid((down.rows + nr - 1) / nr, r.rec ? r.max_rec : 1);
+    const dim3 grid = gemv_grid((down.rows + nr - 1) / nr, r);
     const bool g32 = down.group == 32;
 #define X(G_, L_, T_)                                                                        \
     if (s.gpl == G_ && s.lpr == L_ && tb == T_) {                                            \

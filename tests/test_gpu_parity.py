@@ -231,6 +231,18 @@ def test_layer_f32_fixed_rows_per_expert(E):
     assert rel_l2(out, ref) <= F32_TOL
 
 
+def test_layer_f32_more_pairs_than_a_grid_dimension():
+    # 8200 tokens x top-8 = 65600 pairs: more decode plan records than one
+    # grid dimension holds (65535), so the record index spans grid y and z.
+    say("layer f32 E=16 H=256 F=128 T=8200 k=8 (sampled tokens)")
+    L = Layer(16, 256, 128, seed=29)
+    toks = [0, 1, 4099, 8198, 8199]
+    out, ref = _layer_case(L, 8200, 8, "f32", seed=29, tokens=toks)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= F32_TOL
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_invalid_and_duplicate_ids(dtype):
     say(f"layer invalid/duplicate ids {dtype}")
