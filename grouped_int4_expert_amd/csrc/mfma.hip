@@ -88,11 +88,14 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t *__restrict__
 
 // out[t][n..n+3] = sum over j in pick order of Y[inv[t k + j]][n..n+3]; the
 // four columns share one exponent (n % 4 == 0 stays inside a 16-column block).
+// Token t = blockIdx.z * gridDim.y + blockIdx.y (a grid dimension other than
+// x holds at most 65535 blocks).
 __global__ void __launch_bounds__(256) combine_kernel(YBuf y, const int32_t *__restrict__ inv,
-                                                      int k, int hidden, float *__restrict__ out) {
-    const int t = blockIdx.y;
+                                                      int tokens, int k, int hidden,
+                                                      float *__restrict__ out) {
+    const int t = blockIdx.z * gridDim.y + blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (n >= hidden) return;
+    if (t >= tokens || n >= hidden) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; j++) {
         const int pos = inv[(int64_t)t * k + j];
@@ -120,8 +123,9 @@ hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *
 
 hipError_t launch_combine(YBuf y, const int32_t *inv, int tokens, int k, int hidden, float *out,
                           hipStream_t st) {
-    const dim3 grid((hidden / 4 + 255) / 256, tokens);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, y, inv, k, hidden, out);
+    const int gy = tokens < 65535 ? tokens : 65535;
+    const dim3 grid((hidden / 4 + 255) / 256, gy, (tokens + gy - 1) / gy);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, y, inv, tokens, k, hidden, out);
     return hipGetLastError();
 }
 

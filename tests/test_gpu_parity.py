@@ -243,6 +243,17 @@ def test_layer_f32_more_pairs_than_a_grid_dimension():
     assert err <= F32_TOL
 
 
+def test_layer_bf16_more_tokens_than_a_grid_dimension():
+    # 65600 tokens: the combine's token index spans grid y and z.
+    say("layer bf16 E=8 H=256 F=128 T=65600 k=2 (sampled tokens)")
+    L = Layer(8, 256, 128, seed=30)
+    toks = [0, 1, 65534, 65535, 65536, 65599]
+    out, ref = _layer_case(L, 65600, 2, "bf16", seed=30, tokens=toks)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= BF16_TOL
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_invalid_and_duplicate_ids(dtype):
     say(f"layer invalid/duplicate ids {dtype}")
