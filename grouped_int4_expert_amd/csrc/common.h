@@ -116,7 +116,10 @@ __device__ __forceinline__ float silu_fast(float z) {
 // of I elements: I/32 chunks x 5 planes x 4 dwords (plane k, dword d holds
 // the digits of chunk elements 8d..8d+7, element 8d+i in nibble i), plus one
 // f32 factor 2^(E-18) per chunk in a separate array.  |v| <= 2^18 fits the
-// five-digit range [-559240, 489335].
+// five-digit range [-559240, 489335].  Activation rows (x) take E from the
+// maximum over both chunks of each 64-element group, so the two factors of a
+// group are equal and the fused gate+up kernel combines a group's digit sums
+// once; h (produced 32 features per block) keeps one E per chunk.
 // ---------------------------------------------------------------------------
 constexpr int XD_PLANES = 5;
 constexpr int XD_CHUNK = 32;                       // elements per factor
@@ -126,10 +129,13 @@ constexpr int XD_FRAC_BITS = 18;
 // Quantise one chunk held one element per lane by 32 consecutive lanes
 // (lanes with `valid` false hold zero).  Lane (8d + i) of the chunk gets its
 // five digit nibbles; returns the factor.  Writes plane dwords through
-// `store(plane, dword, value)` from lanes with (lane % 8) == 0.
-template <typename Store>
+// `store(plane, dword, value)` from lanes with (lane % 8) == 0.  PAIR: the
+// two halves of the wave hold the two chunks of one 64-element group and
+// share one exponent (every lane of the wave must take part).
+template <bool PAIR = false, typename Store>
 __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
-    const float m = max32_dpp(fabsf(x));
+    float m = max32_dpp(fabsf(x));
+    if (PAIR) m = fmaxf(m, __shfl_xor(m, 32, QMOE_WAVE));
     float factor;
     int v = 0;
     if (!(m <= 3.0e38f)) {                    // inf or nan in the chunk
@@ -153,6 +159,26 @@ __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
         if (sub == 0) store(k, dw, nib);
     }
     return factor;
+}
+
+// Dot of one 64-element group whose two chunks share the factor `fac`:
+// weights w[0..7] against the digit planes at x[0..39], one digit sum per
+// plane over both chunks and one recombination.  |sum| <= 64 * 8 * 2^18.
+__device__ __forceinline__ float group_dot(const uint32_t *w, const uint32_t *x, float fac) {
+    int s[XD_PLANES];
+#pragma unroll
+    for (int k = 0; k < XD_PLANES; k++) {
+        int a = 0;
+#pragma unroll
+        for (int d = 0; d < 4; d++) a = sdot8(w[d], x[4 * k + d], a);
+#pragma unroll
+        for (int d = 0; d < 4; d++) a = sdot8(w[4 + d], x[XD_DWORDS + 4 * k + d], a);
+        s[k] = a;
+    }
+    int v = s[4];
+#pragma unroll
+    for (int k = 3; k >= 0; k--) v = v * 16 + s[k];
+    return (float)v * fac;
 }
 
 // Dot of one 32-element chunk: weights w[0..3] (two's-complement nibbles)

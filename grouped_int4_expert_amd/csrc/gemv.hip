@@ -151,11 +151,17 @@ __device__ __forceinline__ void load_rows(WReg<GPL, U> &wr, const RowSrc<GPL> &s
     }
 }
 
-template <int GPL, int U, bool G32>
+// PAIRED: the activation's two chunks of each group share one factor
+// (x digits; h digits have one factor per chunk).
+template <int GPL, int U, bool G32, bool PAIRED>
 __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XReg<GPL> &xr) {
     float acc = 0.f;
 #pragma unroll
     for (int gi = 0; gi < GPL; gi++) {
+        if (PAIRED && !G32) {
+            acc = fmaf(wr.s[u][gi][0], group_dot(&wr.w[u][gi][0], &xr.d[gi][0], xr.f[gi][0]), acc);
+            continue;
+        }
         const float g0 = chunk_dot(&wr.w[u][gi][0], &xr.d[gi][0], xr.f[gi][0]);
         const float g1 = chunk_dot(&wr.w[u][gi][4], &xr.d[gi][XD_DWORDS], xr.f[gi][1]);
         if (G32) acc = fmaf(wr.s[u][gi][1], g1, fmaf(wr.s[u][gi][0], g0, acc));
@@ -207,8 +213,8 @@ constexpr int batch_rows() {
 // U rows, the next batch's loads issued before the current batch is
 // computed.  row_at(step) gives the (valid) row index; emit(step, j, value)
 // runs on the last lane of the group.
-template <int GPL, int LPR, int TB, int U, int NSTEP, bool G32, class RowAt, class Prologue,
-          class Emit>
+template <int GPL, int LPR, int TB, int U, int NSTEP, bool G32, bool PAIRED, class RowAt,
+          class Prologue, class Emit>
 __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
                                             const RowSrc<GPL> &src, RowAt row_at,
                                             Prologue prologue, Emit emit) {
@@ -233,7 +239,7 @@ __device__ __forceinline__ void stream_rows(const XReg<GPL> *xr, int nt, int lr,
             if (j < nt) {
 #pragma unroll
                 for (int u = 0; u < U; u++) {
-                    float v = row_dot<GPL, U, G32>(w[b & 1], u, xr[j]);
+                    float v = row_dot<GPL, U, G32, PAIRED>(w[b & 1], u, xr[j]);
                     v = reduce_dpp<LPR>(v);
                     if (lr == LPR - 1) emit(b * U + u, j, v);
                 }
@@ -273,7 +279,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false, G32>(
     for (int t0 = p0; t0 < p1; t0 += TB) {
         const int nt = min(TB, p1 - t0);
         XReg<GPL> xr[TB];
-        stream_rows<GPL, LPR, TB, U, NSTEP, G32>(
+        stream_rows<GPL, LPR, TB, U, NSTEP, G32, true>(
             xr, nt, lr, src, row_at,
             [&]() {
 #pragma unroll
@@ -353,7 +359,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true, G32>()
                 }
             }
         };
-        stream_rows<GPL, LPR, TB, U, NSTEP, G32>(xr, nt, lr, src, row_at, prologue,
+        stream_rows<GPL, LPR, TB, U, NSTEP, G32, false>(xr, nt, lr, src, row_at, prologue,
                                             [&](int step, int j, float v) {
                                                 const int o = row0 + step;
                                                 if (o < O) {

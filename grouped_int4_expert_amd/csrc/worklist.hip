@@ -218,7 +218,7 @@ __device__ void xdigits_chunks(const float *__restrict__ x, int rows, int cols, 
         const int e = (int)ch * XD_CHUNK + sub;
         const float v = e < src_cols ? x[r * src_cols + e] : 0.0f;
         uint32_t *dst = xd.dig + c * XD_DWORDS;
-        const float f = quantise_chunk32(v, [&](int plane, int dw, uint32_t val) {
+        const float f = quantise_chunk32<true>(v, [&](int plane, int dw, uint32_t val) {
             dst[plane * 4 + dw] = val;
         });
         if (sub == 0) xd.fac[c] = f;
