@@ -79,6 +79,15 @@ __device__ __forceinline__ float max16_dpp(float v) {
     return fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v))));
 }
 
+// Unsigned max over each row of 16 lanes, in every lane (DPP only).  For
+// non-negative floats that are not NaN the bit patterns order like the values.
+__device__ __forceinline__ uint32_t max16_u32_dpp(uint32_t v) {
+    v = max(v, dpp_u32<DPP_QUAD_SWAP1>(v));
+    v = max(v, dpp_u32<DPP_QUAD_SWAP2>(v));
+    v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v));
+    return max(v, dpp_u32<DPP_ROW_MIRROR>(v));
+}
+
 // Max over each group of 32 lanes, in every lane: within 16 lanes by DPP
 // (quad pairs, quads, half rows, rows), then one exchange between the two
 // rows.

@@ -96,11 +96,15 @@ __global__ void __launch_bounds__(MF_THREADS, occ_of<BMK>()) mfma_down_kernel(
                     val[rr] = w4[rr] * fr.acc[i][j][4 * g + rr];
                     mx = fmaxf(mx, fabsf(val[rr]));
                 }
-                mx = max16_dpp(mx);
+                // mx >= 0 and never NaN (fmaxf drops NaN), so its bits order
+                // like its value; mx in [2^(ex-1), 2^ex) with ex = exponent
+                // field - 126.  ex is kept in [-111, 127]: 2^(15-ex) and the
+                // combine's 2^(ex-15) stay normal f32 numbers and ex fits int8
+                // (blocks below 2^-111 keep fewer bits; |Y| >= 2^127 saturates).
+                const uint32_t mb = max16_u32_dpp(__float_as_uint(mx));
                 int ex = 0;
-                if (mx > 0.f && mx <= 3.4e38f) frexpf(mx, &ex);   // mx in [2^(ex-1), 2^ex)
-                ex = max(ex, -126);
-                const float sc = ldexpf(1.0f, 15 - ex);
+                if (mb != 0 && mb < 0x7f800000u) ex = min(max((int)(mb >> 23) - 126, -111), 127);
+                const float sc = __uint_as_float((uint32_t)(142 - ex) << 23);   // 2^(15 - ex)
 #pragma unroll
                 for (int rr = 0; rr < 4; rr++)
                     __builtin_amdgcn_raw_buffer_store_b16(

@@ -420,6 +420,21 @@ def test_layer_bf16_outputs_beyond_f16_range():
     assert err <= BF16_TOL
 
 
+def test_layer_bf16_tiny_routing_weights():
+    """Routing weights of ~1e-36 put whole 4 x 16 blocks of the routed down
+    outputs below 2^-111: the block exponent is clamped so that its scale
+    factors stay finite normal f32 numbers, and the outputs keep their
+    relative accuracy."""
+    say("layer bf16 with routing weights x1e-36")
+    L = Layer(8, 512, 256, seed=43)
+    out, ref = _layer_case(L, 50, 2, "bf16", seed=44, mutate=lambda ids, w: (ids, w * 1e-36))
+    assert np.abs(ref).max() < 2.0 ** -100
+    assert np.isfinite(out).all()
+    err = rel_l2(out, ref)
+    say(f"  max |ref| = {np.abs(ref).max():.3e}, rel_l2 = {err:.3e}")
+    assert err <= BF16_TOL
+
+
 def test_layer_wide_topk():
     """k = 16 of 32 experts, f32 and bf16."""
     L = Layer(32, 256, 128, seed=33)
