@@ -171,39 +171,34 @@ __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
 }
 
 // Dot of one 64-element group whose two chunks share the factor `fac`:
-// weights w[0..7] against the digit planes at x[0..39], one digit sum per
-// plane over both chunks and one recombination.  |sum| <= 64 * 8 * 2^18.
+// weights w[0..7] against the digit planes at x[0..39], both chunks of a
+// plane summed in one chain.  The planes are folded in Horner order inside
+// the dot chain (v = 16 v + plane sum), so the chain needs one zero to start
+// and no separate recombination; every partial value is bounded by the full
+// sum, |sum| <= 64 * 8 * 2^18.
 __device__ __forceinline__ float group_dot(const uint32_t *w, const uint32_t *x, float fac) {
-    int s[XD_PLANES];
+    int v = 0;
 #pragma unroll
-    for (int k = 0; k < XD_PLANES; k++) {
-        int a = 0;
+    for (int k = XD_PLANES - 1; k >= 0; k--) {
+        v *= 16;
 #pragma unroll
-        for (int d = 0; d < 4; d++) a = sdot8(w[d], x[4 * k + d], a);
+        for (int d = 0; d < 4; d++) v = sdot8(w[d], x[4 * k + d], v);
 #pragma unroll
-        for (int d = 0; d < 4; d++) a = sdot8(w[4 + d], x[XD_DWORDS + 4 * k + d], a);
-        s[k] = a;
+        for (int d = 0; d < 4; d++) v = sdot8(w[4 + d], x[XD_DWORDS + 4 * k + d], v);
     }
-    int v = s[4];
-#pragma unroll
-    for (int k = 3; k >= 0; k--) v = v * 16 + s[k];
     return (float)v * fac;
 }
 
 // Dot of one 32-element chunk: weights w[0..3] (two's-complement nibbles)
-// against the five digit planes at x[0..19].
+// against the five digit planes at x[0..19], in the same Horner order.
 __device__ __forceinline__ float chunk_dot(const uint32_t *w, const uint32_t *x, float fac) {
-    int s[XD_PLANES];
+    int v = 0;
 #pragma unroll
-    for (int k = 0; k < XD_PLANES; k++) {
-        int a = 0;
+    for (int k = XD_PLANES - 1; k >= 0; k--) {
+        v *= 16;
 #pragma unroll
-        for (int d = 0; d < 4; d++) a = sdot8(w[d], x[4 * k + d], a);
-        s[k] = a;
+        for (int d = 0; d < 4; d++) v = sdot8(w[d], x[4 * k + d], v);
     }
-    int v = s[4];
-#pragma unroll
-    for (int k = 3; k >= 0; k--) v = v * 16 + s[k];
     return (float)v * fac;
 }
 

@@ -170,6 +170,17 @@ __device__ __forceinline__ float row_dot(const WReg<GPL, U> &wr, int u, const XR
     return acc;
 }
 
+// Lane group of this thread (LPR lanes each).  With whole-wave groups it is
+// the wave index, made visibly uniform so that row offsets derived from it
+// stay in scalar registers (a buffer load's scalar offset computed from a
+// value the compiler takes as per-lane is wrapped in a loop over its distinct
+// values).
+template <int LPR>
+__device__ __forceinline__ int lane_group() {
+    if (LPR == 64) return __builtin_amdgcn_readfirstlane(wave_id());
+    return threadIdx.x / LPR;
+}
+
 // Plan record of this block: grid y and z together (a grid dimension other
 // than x holds at most 65535 blocks; there can be one record per pair).
 __device__ __forceinline__ int record_index() { return blockIdx.z * gridDim.y + blockIdx.y; }
@@ -266,7 +277,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, false, G32>(
     if (!block_expert(r, record_index(), e, p0, p1)) return;
     const int H = G.cols, F = G.rows;
     const int ng = H / 64, ncx = H / XD_CHUNK, nch = F / XD_CHUNK;
-    const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
+    const int lr = threadIdx.x % LPR, slot = lane_group<LPR>();
     const int row0 = blockIdx.x * 32;
     // Row tasks 0..63 are the 32 gate rows then the same 32 up rows; every
     // wave owns 16 consecutive tasks (NSTEP rows for each of its 64/LPR lane
@@ -330,7 +341,7 @@ __global__ void __launch_bounds__(GV_THREADS, (gv_occ<GPL, LPR, TB, true, G32>()
     if (!block_expert(r, record_index(), e, p0, p1)) return;
     const int O = D.rows, I = D.cols;
     const int ng = I / 64, ncx = I / XD_CHUNK;
-    const int lr = threadIdx.x % LPR, slot = threadIdx.x / LPR;
+    const int lr = threadIdx.x % LPR, slot = lane_group<LPR>();
     const int row0 = blockIdx.x * NR + slot * NSTEP;
     const bool routed = r.rec != nullptr;
     const RowSrc<GPL> src = row_src<GPL, LPR, G32>(D, e, lr);
