@@ -53,7 +53,9 @@ def test_matvec_random(group):
 
 
 @pytest.mark.parametrize("group", GROUPS)
-@pytest.mark.parametrize("dtype,T,k", [("f32", 23, 4), ("bf16", 23, 4), ("bf16", 700, 2)])
+# f32 23 x 4 over 16 experts: two tokens per gate+up pass; 3 x 2: one.
+@pytest.mark.parametrize("dtype,T,k", [("f32", 23, 4), ("f32", 3, 2), ("bf16", 23, 4),
+                                       ("bf16", 700, 2)])
 def test_layer_groups(group, dtype, T, k):
     E, H, F = 4 if T > 100 else 16, 512, 256
     gs = _gs(group, max(H, F))
