@@ -274,9 +274,10 @@ size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
  * and must not overlap x, the routing arrays or the workspace.  Routing is
  * an input: the layer does not pick experts.  Ids outside [0, E) are
  * dropped.  After the call the workspace begins with the worklist in the
- * layout of qmoe_layer_ws_view (for inspection and tests).  Each expert's
- * weights are streamed once per call on the decode path (all of that
- * expert's tokens share the pass). */
+ * layout of qmoe_layer_ws_view (for inspection and tests).  On the decode
+ * path an expert's tokens are taken one or two per weight pass; the passes
+ * of one expert run side by side, so its weights come from HBM about once
+ * per call and the later passes read them from the L2 cache. */
 int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
                int32_t tokens, const int32_t *topk_ids, const float *topk_w,
                int32_t k, float *out, void *ws, size_t ws_bytes, void *stream);
