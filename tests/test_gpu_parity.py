@@ -255,6 +255,17 @@ def test_layer_bf16_more_tokens_than_a_grid_dimension():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_every_pair_on_one_expert(dtype):
+    # 40 tokens x 4 slots all routed to expert 3 (duplicates within a token
+    # included): one expert with 160 pairs, the others idle.
+    say(f"layer E=8 H=256 F=128 T=40 k=4 {dtype}, every pair on expert 3")
+    L = Layer(8, 256, 128, seed=31)
+    out, ref = _layer_case(L, 40, 4, dtype, seed=31,
+                           mutate=lambda ids, w: (torch.full_like(ids, 3), w))
+    assert rel_l2(out, ref) <= (F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_layer_invalid_and_duplicate_ids(dtype):
     say(f"layer invalid/duplicate ids {dtype}")
     L = Layer(8, 256, 128, seed=22)
