@@ -183,7 +183,10 @@ __device__ __forceinline__ void mfma_mainloop(Frags<MF> &fr, const LoopSrc<MF> &
                                               uint16_t *__restrict__ s3) {
     static_assert(MFC <= MF, "row fragments");
     constexpr int LPG = MFC + 2 * NF;   // loads per thread per group, in issue order
-    constexpr int VALU_PER_MFMA = (40 + MFC * NF - 1) / (MFC * NF);
+    // VALU slots the scheduler may place after each MFMA: a k-step has about
+    // 31 VALU instructions (two 8-code unpacks and the scale conversion); a
+    // budget of 32 per k-step measured 1-2 % faster than 40 or 64.
+    constexpr int VALU_PER_MFMA = (32 + MFC * NF - 1) / (MFC * NF);
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int hh = lane >> 5, nl = lane & 31;
