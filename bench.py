@@ -398,8 +398,6 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
-                    help="time only part of the step (for counter runs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the router, host-expert and group-size timings that run "
                          "after the step (for profiler runs)")
@@ -525,13 +523,7 @@ def main():
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        if args.only != "prefill":
-            graph.replay()
-        if args.only == "decode":
-            if evs is not None:
-                for ev in evs[1:]:
-                    ev.record()
-            return
+        graph.replay()
         if evs is not None:
             qm.qmoe_layer_ex(pre_layer, xp_d, ip_d, wp_d, evs[1:], out=out_p, ws=ws_p)
         else:
