@@ -25,7 +25,8 @@ QMOE_F32 = 0
 QMOE_BF16 = 1
 STATUS = {0: "QMOE_OK", 1: "QMOE_ERR_NULL", 2: "QMOE_ERR_SHAPE", 3: "QMOE_ERR_ALIGN",
           4: "QMOE_ERR_UNSUPPORTED", 5: "QMOE_ERR_WORKSPACE", 6: "QMOE_ERR_ALIAS",
-          7: "QMOE_ERR_ABI", 8: "QMOE_ERR_HIP"}
+          7: "QMOE_ERR_ABI", 8: "QMOE_ERR_HIP", 9: "QMOE_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class QmoeError(RuntimeError):
@@ -61,7 +62,7 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route",
            "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
            "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_layer_logits_workspace_bytes",
-           "qmoe_layer_logits"]
+           "qmoe_layer_logits", "qmoe_layer_noalloc"]
 
 _lib = None
 
@@ -111,6 +112,8 @@ def load(path: str | None = None):
         "qmoe_layer_logits_workspace_bytes": (sz, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32]),
         "qmoe_layer_logits": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, i32,
                                              vp, vp, sz, vp]),
+        "qmoe_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp,
+                                              vp, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -428,6 +431,23 @@ def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=Non
     _check(load().qmoe_layer(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
                              _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
            "qmoe_layer")
+    return o
+
+
+def qmoe_layer_noalloc(layer: QLayer, x, topk_ids, topk_w, out=None, stream=None):
+    """qmoe_layer without a workspace argument: the library's fixed device
+    scratch (NOALLOC_SCRATCH_BYTES per GPU) serves as the workspace, so the
+    call allocates nothing beyond `out` (pass `out` to allocate nothing)."""
+    _dev(x, "x")
+    _dev(topk_ids, "topk_ids", torch.int32)
+    _dev(topk_w, "topk_w", torch.float32)
+    code = _dtype_code(x)
+    T, k = topk_ids.shape
+    o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
+                                                device=x.device)
+    _check(load().qmoe_layer_noalloc(ctypes.byref(layer.desc), code, _ptr(x), T,
+                                     _ptr(topk_ids), _ptr(topk_w), k, _ptr(o),
+                                     _stream(stream)), "qmoe_layer_noalloc")
     return o
 
 

@@ -202,6 +202,9 @@ const char *qmoe_status_str(int status) {
         case QMOE_ERR_ALIAS: return "output overlaps an input or the workspace";
         case QMOE_ERR_ABI: return "struct_size mismatch (library and caller built from different headers)";
         case QMOE_ERR_HIP: return "HIP launch failed";
+        case QMOE_ERR_SCRATCH:
+            return "needs more workspace than the allocation-free entry point's fixed scratch "
+                   "(QMOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

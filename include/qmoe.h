@@ -70,7 +70,8 @@ enum {
     QMOE_ERR_WORKSPACE = 5,   /* workspace missing or too small */
     QMOE_ERR_ALIAS = 6,       /* an output overlaps an input */
     QMOE_ERR_ABI = 7,         /* struct_size does not match this library */
-    QMOE_ERR_HIP = 8          /* a kernel launch failed (hipGetLastError) */
+    QMOE_ERR_HIP = 8,         /* a kernel launch failed (hipGetLastError) */
+    QMOE_ERR_SCRATCH = 9      /* more than qmoe_layer_noalloc's fixed scratch */
 };
 
 /* Activation dtypes.  The dtype of x selects the path: f32 = decode (GEMV
@@ -317,6 +318,28 @@ typedef struct qmoe_layer_ws_view {
 } qmoe_layer_ws_view;
 int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens,
                          int32_t k, int32_t x_dtype, qmoe_layer_ws_view *view);
+
+/* Allocation-free variant of qmoe_layer, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and checks as
+ * qmoe_layer, without ws/ws_bytes: the workspace is a fixed device array of
+ * QMOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call runs on the current device; its first call on a
+ * device looks up that device's array (no allocation), later calls reuse it.
+ * Nothing is allocated or freed and nothing in the array needs to start at
+ * zero.  A call whose qmoe_layer_workspace_bytes exceeds the array returns
+ * QMOE_ERR_SCRATCH and launches nothing (at hidden 4096, intermediate 1536
+ * and top-8, the 64 MiB hold the f32 path up to about 1,500 tokens and the
+ * bf16 path up to about 650 tokens).  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams, or different host threads without ordering) race
+ * and give wrong results; calls serialised on one stream are safe.  After a
+ * call the array begins with the worklist in the layout of
+ * qmoe_layer_ws_layout, as a qmoe_layer workspace does. */
+#define QMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int qmoe_layer_noalloc(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
+                       int32_t tokens, const int32_t *topk_ids, const float *topk_w,
+                       int32_t k, float *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status(lib):
     assert lib.qmoe_abi_version() == q.ABI_VERSION == 1
-    for s in range(9):
+    for s in range(10):
         assert q.qmoe_status_str(s)
     assert q.qmoe_status_str(999) == "unknown status"
 
@@ -258,3 +258,21 @@ def test_layer_logits_validation(lib):
     assert lib.qmoe_layer_logits(ctypes.byref(d), 0, None, T, L, k, O, W, nb, None) == 1
     assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, T, L, k, X, W, nb, None) == 6
     assert lib.qmoe_layer_logits(ctypes.byref(d), 0, X, 0, None, k, None, None, 0, None) == 0
+
+
+def test_layer_noalloc_rejections(lib):
+    """The allocation-free layer refuses, before touching any device, a stale
+    descriptor, bad sizes and a call whose workspace exceeds its fixed scratch."""
+    def call(d, dtype=0, T=2, k=2):
+        return lib.qmoe_layer_noalloc(ctypes.byref(d), dtype, FAKE + (6 << 32), T,
+                                      FAKE + (7 << 32), FAKE + (8 << 32), k,
+                                      FAKE + (9 << 32), None)
+    assert call(layer_desc(size=8)) == 7
+    assert call(layer_desc(), k=0) == 2
+    assert call(layer_desc(), T=-1) == 2
+    assert call(layer_desc(), dtype=7) == 4
+    big = layer_desc(E=4, H=4096, F=1536)
+    need = lib.qmoe_layer_workspace_bytes(ctypes.byref(big), 4096, 8, 1)
+    assert need > q.NOALLOC_SCRATCH_BYTES
+    assert call(big, dtype=1, T=4096, k=8) == 9
+    assert q.qmoe_status_str(9).startswith("needs more workspace")
