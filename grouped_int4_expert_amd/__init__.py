@@ -23,6 +23,7 @@ ABI_VERSION = 1
 QMOE_OK = 0
 QMOE_F32 = 0
 QMOE_BF16 = 1
+QMOE_F32_DIGITS = 2      # f32 x, activations rounded to 18-bit block fixed point
 STATUS = {0: "QMOE_OK", 1: "QMOE_ERR_NULL", 2: "QMOE_ERR_SHAPE", 3: "QMOE_ERR_ALIGN",
           4: "QMOE_ERR_UNSUPPORTED", 5: "QMOE_ERR_WORKSPACE", 6: "QMOE_ERR_ALIAS",
           7: "QMOE_ERR_ABI", 8: "QMOE_ERR_HIP", 9: "QMOE_ERR_SCRATCH"}
@@ -313,7 +314,15 @@ class ExpertCache:
             pass
 
 
-def _dtype_code(x):
+def _dtype_code(x, x_dtype=None):
+    """Path code from x's dtype: float32 -> QMOE_F32 (f32 arithmetic), bfloat16
+    -> QMOE_BF16.  x_dtype=QMOE_F32_DIGITS selects the digit variant of the
+    f32 path (x still float32)."""
+    if x_dtype is not None:
+        want = torch.bfloat16 if x_dtype == QMOE_BF16 else torch.float32
+        if x.dtype != want:
+            raise TypeError(f"x_dtype {x_dtype} needs x of {want}, got {x.dtype}")
+        return int(x_dtype)
     if x.dtype == torch.float32:
         return QMOE_F32
     if x.dtype == torch.bfloat16:
@@ -321,12 +330,22 @@ def _dtype_code(x):
     raise TypeError("x must be float32 (decode path) or bfloat16 (prefill path)")
 
 
-def _workspace(nbytes, device, ws):
+def _workspace(nbytes, device, ws, stream=None):
+    """The caller's workspace, or a new one.  A new one is allocated by
+    torch's caching allocator; when the call runs on a stream other than the
+    current one, the block is marked as used by that stream so that it is not
+    handed out again before the call's kernels have finished with it."""
     if ws is not None:
         if ws.numel() < nbytes:
             raise ValueError(f"workspace of {ws.numel()} bytes < {nbytes}")
         return ws
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    t = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if stream is not None:
+        st = stream if isinstance(stream, torch.cuda.Stream) else \
+            torch.cuda.ExternalStream(int(stream), device=device)
+        if st != torch.cuda.current_stream(device):
+            t.record_stream(st)
+    return t
 
 
 # ------------------------------------------------------------------ calls ---
@@ -340,17 +359,17 @@ def qmoe_matvec(pq, s, cols, x, group=64, out=None, ws=None, stream=None):
     y = out if out is not None else torch.empty(batch, W.rows, dtype=torch.float32,
                                                 device=x.device)
     nb = int(load().qmoe_matvec_workspace_bytes(ctypes.byref(W), batch))
-    ws = _workspace(nb, x.device, ws)
+    ws = _workspace(nb, x.device, ws, stream)
     _check(load().qmoe_matvec(ctypes.byref(W), _ptr(x), batch, _ptr(y), _ptr(ws), ws.numel(),
                               _stream(stream)), "qmoe_matvec")
     return y
 
 
 def qmoe_expert_ffn(pg, sg, pu, su, pd, sd, hidden, inter, x, group=64, out=None, ws=None,
-                    stream=None):
+                    stream=None, x_dtype=None):
     """out = down(silu(gate x) * (up x)) for one expert; x f32 or bf16 [B, H]."""
     _dev(x, "x")
-    code = _dtype_code(x)
+    code = _dtype_code(x, x_dtype)
     G = make_qmat(pg, sg, hidden, group)
     U = make_qmat(pu, su, hidden, group)
     D = make_qmat(pd, sd, inter, group)
@@ -359,7 +378,7 @@ def qmoe_expert_ffn(pg, sg, pu, su, pd, sd, hidden, inter, x, group=64, out=None
                                                 device=x.device)
     nb = int(load().qmoe_expert_ffn_workspace_bytes(ctypes.byref(G), ctypes.byref(U),
                                                     ctypes.byref(D), code, batch))
-    ws = _workspace(nb, x.device, ws)
+    ws = _workspace(nb, x.device, ws, stream)
     _check(load().qmoe_expert_ffn(ctypes.byref(G), ctypes.byref(U), ctypes.byref(D), code,
                                   _ptr(x), batch, _ptr(o), _ptr(ws), ws.numel(),
                                   _stream(stream)), "qmoe_expert_ffn")
@@ -378,7 +397,7 @@ def qmoe_worklist(topk_ids, experts, ws=None, stream=None):
                inv=torch.empty(max(n, 1), dtype=torch.int32, device=dev),
                n_invalid=torch.empty(1, dtype=torch.int32, device=dev))
     nb = int(load().qmoe_worklist_workspace_bytes(T, k, experts))
-    ws = _workspace(nb, dev, ws)
+    ws = _workspace(nb, dev, ws, stream)
     _check(load().qmoe_worklist(_ptr(topk_ids), T, k, experts, _ptr(out["counts"]),
                                 _ptr(out["offsets"]), _ptr(out["pairs"]), _ptr(out["inv"]),
                                 _ptr(out["n_invalid"]), _ptr(ws), ws.numel(),
@@ -417,31 +436,33 @@ def qmoe_route(logits, k, ids=None, w=None, stream=None):
     return ids, w
 
 
-def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=None):
+def qmoe_layer(layer: QLayer, x, topk_ids, topk_w, out=None, ws=None, stream=None,
+               x_dtype=None):
     """Routed MoE layer: out[t] = sum_j w[t,j] * ffn_{ids[t,j]}(x_t)."""
     _dev(x, "x")
     _dev(topk_ids, "topk_ids", torch.int32)
     _dev(topk_w, "topk_w", torch.float32)
-    code = _dtype_code(x)
+    code = _dtype_code(x, x_dtype)
     T, k = topk_ids.shape
     o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
                                                 device=x.device)
     nb = layer.workspace_bytes(T, k, code)
-    ws = _workspace(nb, x.device, ws)
+    ws = _workspace(nb, x.device, ws, stream)
     _check(load().qmoe_layer(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),
                              _ptr(topk_w), k, _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
            "qmoe_layer")
     return o
 
 
-def qmoe_layer_noalloc(layer: QLayer, x, topk_ids, topk_w, out=None, stream=None):
+def qmoe_layer_noalloc(layer: QLayer, x, topk_ids, topk_w, out=None, stream=None,
+                       x_dtype=None):
     """qmoe_layer without a workspace argument: the library's fixed device
     scratch (NOALLOC_SCRATCH_BYTES per GPU) serves as the workspace, so the
     call allocates nothing beyond `out` (pass `out` to allocate nothing)."""
     _dev(x, "x")
     _dev(topk_ids, "topk_ids", torch.int32)
     _dev(topk_w, "topk_w", torch.float32)
-    code = _dtype_code(x)
+    code = _dtype_code(x, x_dtype)
     T, k = topk_ids.shape
     o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
                                                 device=x.device)
@@ -451,17 +472,18 @@ def qmoe_layer_noalloc(layer: QLayer, x, topk_ids, topk_w, out=None, stream=None
     return o
 
 
-def qmoe_layer_logits(layer: QLayer, x, logits, k, out=None, ws=None, stream=None):
+def qmoe_layer_logits(layer: QLayer, x, logits, k, out=None, ws=None, stream=None,
+                      x_dtype=None):
     """Router + layer in one call: route f32 logits [T, E] on the device, then
     out[t] = sum_j w[t,j] * ffn_{ids[t,j]}(x_t)."""
     _dev(x, "x")
     _dev(logits, "logits", torch.float32)
-    code = _dtype_code(x)
+    code = _dtype_code(x, x_dtype)
     T = x.shape[0]
     o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
                                                 device=x.device)
     nb = int(load().qmoe_layer_logits_workspace_bytes(ctypes.byref(layer.desc), T, k, code))
-    ws = _workspace(nb, x.device, ws)
+    ws = _workspace(nb, x.device, ws, stream)
     _check(load().qmoe_layer_logits(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(logits), k,
                                     _ptr(o), _ptr(ws), ws.numel(), _stream(stream)),
            "qmoe_layer_logits")
@@ -469,16 +491,16 @@ def qmoe_layer_logits(layer: QLayer, x, logits, k, out=None, ws=None, stream=Non
 
 
 def qmoe_layer_ex(layer: QLayer, x, topk_ids, topk_w, events, out=None, ws=None,
-                  stream=None):
+                  stream=None, x_dtype=None):
     """qmoe_layer that records the given torch.cuda.Event objects between its
     phases (events[0] before the first kernel)."""
     _dev(x, "x")
-    code = _dtype_code(x)
+    code = _dtype_code(x, x_dtype)
     T, k = topk_ids.shape
     o = out if out is not None else torch.empty(T, layer.hidden, dtype=torch.float32,
                                                 device=x.device)
     nb = layer.workspace_bytes(T, k, code)
-    ws = _workspace(nb, x.device, ws)
+    ws = _workspace(nb, x.device, ws, stream)
     handles = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(ev.cuda_event)
                                                   for ev in events])
     _check(load().qmoe_layer_ex(ctypes.byref(layer.desc), code, _ptr(x), T, _ptr(topk_ids),

@@ -13,6 +13,18 @@ bool gemv_supported(int cols);
 }
 
 namespace {
+// f32 activations: QMOE_F32 (f32 arithmetic) or QMOE_F32_DIGITS (the
+// block fixed-point digit variant); both read x as f32 [tokens][H].
+inline bool is_f32(int dtype) { return dtype == QMOE_F32 || dtype == QMOE_F32_DIGITS; }
+inline int x_elem_bytes(int dtype) { return is_f32(dtype) ? 4 : 2; }
+// Widths the decode kernels of a dtype take (hidden into gate+up, inter into down).
+inline bool decode_widths_ok(int dtype, int H, int F) {
+    if (dtype == QMOE_F32) return f32_gateup_supported(H) && f32_down_supported(F);
+    return gemv_supported(H) && gemv_supported(F);
+}
+}  // namespace
+
+namespace {
 
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 64;
@@ -111,6 +123,7 @@ struct LayerWs {
     int32_t *hist;
     XDigits xd, hd;
     DecodePlan plan;
+    float *hf;           // f32 path: h [pairs][F]
     uint16_t *x16, *h16;
     float *xinv;
     YBuf y;
@@ -137,6 +150,15 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
     L.wl.tile_m = MFMA_BM;
     L.hist = c.take<int32_t>(wl_scratch_ints(n, E));
     if (dtype == QMOE_F32) {
+        if (n > F32_INLINE_MAX) {
+            L.plan.rec_gu = c.take<int32_t>(4 * n);
+            L.plan.rec_dn = c.take<int32_t>(4 * n);
+            L.plan.tok = c.take<int32_t>(n);
+            L.plan.wsort = c.take<float>(n);
+            L.plan.max_rec = (int)n;
+        }
+        L.hf = c.take<float>(n * F);
+    } else if (dtype == QMOE_F32_DIGITS) {
         L.plan.rec_gu = c.take<int32_t>(4 * n);
         L.plan.rec_dn = c.take<int32_t>(4 * n);
         L.plan.tok = c.take<int32_t>(n);
@@ -266,8 +288,6 @@ size_t qmoe_matvec_workspace_bytes(const qmoe_qmat *W, int32_t batch) {
     if (!W || batch < 0 || W->cols <= 0 || W->rows <= 0 || W->group <= 0) return 0;
     const MatvecPlan p = matvec_plan(W);
     Carver c(nullptr);
-    c.take<uint32_t>((int64_t)batch * (p.cols / 32) * 20);
-    c.take<float>((int64_t)batch * (p.cols / 32));
     if (p.relaid) {
         c.take<uint8_t>((int64_t)W->rows * (p.cols / 2));
         c.take<float>((int64_t)W->rows * p.ng);
@@ -282,7 +302,7 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     if (batch < 0 || W->rows <= 0 || W->cols <= 0 || W->group <= 0) return QMOE_ERR_SHAPE;
     if (!group_supported(W->group, W->cols)) return QMOE_ERR_UNSUPPORTED;
     const MatvecPlan p = matvec_plan(W);
-    if (!gemv_supported((int)p.cols) || !gemv_fits(W->rows, p.cols, p.group))
+    if (!f32_down_supported((int)p.cols) || !gemv_fits(W->rows, p.cols, p.group))
         return QMOE_ERR_UNSUPPORTED;
     if (!W->q || !W->s) return QMOE_ERR_NULL;
     if (!aligned16(W->q) || !aligned16(W->s)) return QMOE_ERR_ALIGN;
@@ -290,8 +310,8 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
     if (!x || !y) return QMOE_ERR_NULL;
     if (!aligned16(x) || !aligned16(y)) return QMOE_ERR_ALIGN;
     const size_t need = qmoe_matvec_workspace_bytes(W, batch);
-    if (!ws || ws_bytes < need) return QMOE_ERR_WORKSPACE;
-    if (!aligned16(ws)) return QMOE_ERR_ALIGN;
+    if (need > 0 && (!ws || ws_bytes < need)) return QMOE_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return QMOE_ERR_ALIGN;
     const int64_t xb = (int64_t)batch * W->cols * 4, yb = (int64_t)batch * W->rows * 4;
     if (overlap(y, yb, x, xb) || overlap(y, yb, ws, need) || overlap(x, xb, ws, need) ||
         overlap(y, yb, W->q, packed_bytes(W->rows, W->cols)) ||
@@ -300,9 +320,6 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
         overlap(ws, need, W->s, 4 * scale_count(W->rows, W->cols, W->group)))
         return QMOE_ERR_ALIAS;
     Carver c(ws);
-    XDigits xd;
-    xd.dig = c.take<uint32_t>((int64_t)batch * (p.cols / 32) * 20);
-    xd.fac = c.take<float>((int64_t)batch * (p.cols / 32));
     const hipStream_t st = as_stream(stream);
     QMat M = to_qmat(W);
     hipError_t e = hipSuccess;
@@ -315,8 +332,10 @@ int qmoe_matvec(const qmoe_qmat *W, const float *x, int32_t batch, float *y, voi
         M.cols = (int)p.cols;
         M.group = (int)p.group;
     }
-    if (e == hipSuccess) e = launch_xdigits(x, batch, (int)p.cols, W->cols, xd, st);
-    if (e == hipSuccess) e = launch_gemv_matvec(M, xd, batch, y, st);
+    F32Route r{};
+    r.ntok = batch;
+    const int tb = batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
+    if (e == hipSuccess) e = launch_f32_down(M, x, W->cols, W->cols, y, r, tb, false, st);
     return status_of(e);
 }
 
@@ -328,6 +347,8 @@ size_t qmoe_expert_ffn_workspace_bytes(const qmoe_qmat *gate, const qmoe_qmat *u
     const int64_t H = gate->cols, F = gate->rows;
     Carver c(nullptr);
     if (x_dtype == QMOE_F32) {
+        c.take<float>(batch * F);
+    } else if (x_dtype == QMOE_F32_DIGITS) {
         c.take<uint32_t>(batch * (H / 32) * 20);
         c.take<float>(batch * (H / 32));
         c.take<uint32_t>(batch * (F / 32) * 20);
@@ -354,9 +375,8 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     if ((s = check_qmat(up, F, H, 1))) return s;
     if ((s = check_qmat(down, H, F, 1))) return s;
     if (gate->group != up->group) return QMOE_ERR_SHAPE;   // one fused gate+up pass
-    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
-    if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
-        return QMOE_ERR_UNSUPPORTED;
+    if (!is_f32(x_dtype) && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (is_f32(x_dtype) && !decode_widths_ok(x_dtype, H, F)) return QMOE_ERR_UNSUPPORTED;
     if (x_dtype == QMOE_BF16 && H % 64 != 0) return QMOE_ERR_UNSUPPORTED;
     if (batch == 0) return QMOE_OK;
     if (!x || !out) return QMOE_ERR_NULL;
@@ -364,7 +384,7 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     const size_t need = qmoe_expert_ffn_workspace_bytes(gate, up, down, x_dtype, batch);
     if (!ws || ws_bytes < need) return QMOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return QMOE_ERR_ALIGN;
-    const int64_t xb = (int64_t)batch * H * (x_dtype == QMOE_F32 ? 4 : 2);
+    const int64_t xb = (int64_t)batch * H * x_elem_bytes(x_dtype);
     const int64_t ob = (int64_t)batch * H * 4;
     if (overlap(out, ob, x, xb) || overlap(out, ob, ws, need) || overlap(x, xb, ws, need))
         return QMOE_ERR_ALIAS;
@@ -372,6 +392,14 @@ int qmoe_expert_ffn(const qmoe_qmat *gate, const qmoe_qmat *up, const qmoe_qmat 
     Carver c(ws);
     hipError_t e;
     if (x_dtype == QMOE_F32) {
+        float *hf = c.take<float>((int64_t)batch * F);
+        F32Route r{};
+        r.ntok = batch;
+        const int tb = batch >= 4 ? 4 : batch >= 2 ? 2 : 1;
+        e = launch_f32_gateup(to_qmat(gate), to_qmat(up), static_cast<const float *>(x), hf, r,
+                              tb, st);
+        if (e == hipSuccess) e = launch_f32_down(to_qmat(down), hf, F, F, out, r, tb, false, st);
+    } else if (x_dtype == QMOE_F32_DIGITS) {
         XDigits xd, hd;
         xd.dig = c.take<uint32_t>((int64_t)batch * (H / 32) * 20);
         xd.fac = c.take<float>((int64_t)batch * (H / 32));
@@ -478,7 +506,7 @@ int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k, int32_t ex
 size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens, int32_t k,
                                   int32_t x_dtype) {
     if (!desc || tokens < 0 || k < 1 || desc->experts < 1) return 0;
-    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return 0;
+    if (!is_f32(x_dtype) && x_dtype != QMOE_BF16) return 0;
     return (size_t)carve_layer(nullptr, desc->experts, desc->hidden, desc->inter, tokens, k,
                                x_dtype)
         .bytes;
@@ -510,12 +538,11 @@ static int layer_validate(const qmoe_layer_desc *desc, int32_t x_dtype, const vo
                           int32_t n_events) {
     int s = check_layer_desc(desc);
     if (s) return s;
-    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (!is_f32(x_dtype) && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
     if (tokens < 0 || k < 1 || k > MAX_TOPK) return QMOE_ERR_SHAPE;
     if ((int64_t)tokens * k > (int64_t)1 << 30) return QMOE_ERR_SHAPE;
     const int E = desc->experts, H = desc->hidden, F = desc->inter;
-    if (x_dtype == QMOE_F32 && (!gemv_supported(H) || !gemv_supported(F)))
-        return QMOE_ERR_UNSUPPORTED;
+    if (is_f32(x_dtype) && !decode_widths_ok(x_dtype, H, F)) return QMOE_ERR_UNSUPPORTED;
     if (x_dtype == QMOE_BF16 && H % 64 != 0) return QMOE_ERR_UNSUPPORTED;
     {
         const int64_t n0 = (int64_t)tokens * k;
@@ -524,8 +551,8 @@ static int layer_validate(const qmoe_layer_desc *desc, int32_t x_dtype, const vo
         if (x_dtype == QMOE_BF16 && !mfma_fits(H, F, tokens, n0)) return QMOE_ERR_SHAPE;
     }
     if (phase_events) {
-        if (n_events < (x_dtype == QMOE_F32 ? 4 : 5)) return QMOE_ERR_SHAPE;
-        for (int i = 0; i < (x_dtype == QMOE_F32 ? 4 : 5); i++)
+        if (n_events < (is_f32(x_dtype) ? 4 : 5)) return QMOE_ERR_SHAPE;
+        for (int i = 0; i < (is_f32(x_dtype) ? 4 : 5); i++)
             if (!phase_events[i]) return QMOE_ERR_NULL;
     }
     if (tokens == 0) return QMOE_OK;
@@ -536,7 +563,7 @@ static int layer_validate(const qmoe_layer_desc *desc, int32_t x_dtype, const vo
     if (!ws || (int64_t)ws_bytes < need.bytes) return QMOE_ERR_WORKSPACE;
     if (!aligned16(ws)) return QMOE_ERR_ALIGN;
     const int64_t n = (int64_t)tokens * k;
-    const int64_t xb = (int64_t)tokens * H * (x_dtype == QMOE_F32 ? 4 : 2);
+    const int64_t xb = (int64_t)tokens * H * x_elem_bytes(x_dtype);
     const int64_t ob = (int64_t)tokens * H * 4;
     if (overlap(out, ob, x, xb) || overlap(out, ob, topk_ids, 4 * n) ||
         overlap(out, ob, topk_w, 4 * n) || overlap(out, ob, ws, need.bytes) ||
@@ -566,6 +593,46 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
     hipError_t e = mark();
     if (e != hipSuccess) return QMOE_ERR_HIP;
     if (x_dtype == QMOE_F32) {
+        const int tb_gu = f32_tokens_per_pass((int)n, E, true);
+        const int tb_dn = f32_tokens_per_pass((int)n, E, false);
+        F32Route r{};
+        r.k = k;
+        r.E = E;
+        r.n = (int)n;
+        if (n <= F32_INLINE_MAX) {
+            // the gate+up launch groups the pairs itself; its leading grid
+            // row writes the worklist view and clears out
+            r.ids = topk_ids;
+            r.topk_w = topk_w;
+            r.lead_row = 1;
+            r.wl = L.wl;
+            r.out = out;
+            r.out_tokens = tokens;
+            r.out_cols = H;
+            if (e == hipSuccess) e = mark();
+        } else {
+            Worklist wl = L.wl;
+            wl.tiles = nullptr;
+            wl.n_tiles = nullptr;
+            DecodePlan plan = L.plan;
+            plan.tb_gu = tb_gu;
+            plan.tb_dn = tb_dn;
+            e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, plan,
+                                   static_cast<const float *>(x), tokens, H, XDigits{}, out, st);
+            if (e == hipSuccess) e = mark();
+            r.rec = plan.rec_gu;
+            r.tok = plan.tok;
+            r.wsort = plan.wsort;
+            r.max_rec = plan.max_rec;
+        }
+        if (e == hipSuccess)
+            e = launch_f32_gateup(G, U, static_cast<const float *>(x), L.hf, r, tb_gu, st);
+        if (e == hipSuccess) e = mark();
+        r.lead_row = 0;
+        if (r.rec) r.rec = L.plan.rec_dn;
+        if (e == hipSuccess) e = launch_f32_down(D, L.hf, F, F, out, r, tb_dn, true, st);
+        if (e == hipSuccess) e = mark();
+    } else if (x_dtype == QMOE_F32_DIGITS) {
         Worklist wl = L.wl;
         wl.tiles = nullptr;
         wl.n_tiles = nullptr;

@@ -145,9 +145,14 @@ template <bool PAIR = false, typename Store>
 __device__ __forceinline__ float quantise_chunk32(float x, Store store) {
     float m = max32_dpp(fabsf(x));
     if (PAIR) m = fmaxf(m, __shfl_xor(m, 32, QMOE_WAVE));
+    // fmaxf drops NaN, so NaN is found on its own: a ballot over the chunk's
+    // lanes (both halves of the wave for PAIR)
+    const uint64_t nan_lanes = __ballot(x != x);
+    const bool any_nan =
+        PAIR ? nan_lanes != 0ull : ((nan_lanes >> (lane_id() & 32)) & 0xffffffffull) != 0ull;
     float factor;
     int v = 0;
-    if (!(m <= 3.0e38f)) {                    // inf or nan in the chunk
+    if (any_nan || !(m <= 3.0e38f)) {         // NaN or inf in the chunk: no digits
         factor = __int_as_float(0x7fc00000);
     } else if (m == 0.0f) {
         factor = 0.0f;

@@ -1,0 +1,573 @@
+// Decode GEMVs in f32 arithmetic (f32 activations): grouped int4 weights are
+// streamed once per expert with 128-bit buffer loads, every code is unpacked
+// in registers to an exact f32, multiplied with the f32 activation in an f32
+// FMA chain, scaled once per group by its f32 scale and reduced across lanes
+// with DPP.
+//
+// What is computed follows the colibri pull request "cuda+engine: full fmt=4
+// (grouped int4 gs=64) support": the per-group scale scales[o*ng + i/gs]
+// applied once per group (comment "blocked by GPU driver instability": the
+// grouped kernel accumulates a group and then applies its scale), and the
+// fused gate+up pair that loads the activation once for both matrices
+// (Summary, "matmul_i4_grouped_pair").  The routed layer's tokens are grouped
+// by expert on the device, with no host round trip (pxq_llama.cpp release
+// notes, "Device-side MoE row map").
+//
+// MI355X mapping.  A lane owns one 32-input chunk of a row (16 packed bytes,
+// one 128-bit load per row) and keeps that chunk of each token's activation
+// in 32 registers, so activations are read once per block and weights stream
+// past them.  L lanes (16, 32 or 64: one, two or four DPP rows) cover L
+// chunks of a row; a row of C chunks is split into S slices of L chunks, one
+// wave per slice, and a wave instruction covers 64/L rows.  A 32-input chunk
+// lies inside one scale group for every supported group size (32, 64 * 2^j,
+// one per row), so each lane needs one scale per row, at index
+// (32 * chunk) >> log2(group).
+//
+// Unpack: with w' = w ^ 0x88888888 (offset nibbles -> two's complement),
+// (w' & 0xF0F0F0F0) holds 16*q of the odd elements as signed bytes and
+// ((w' << 4) & 0xF0F0F0F0) 16*q of the even ones; each byte converts to f32
+// in one sign-extending instruction, and the factor 16 (a power of two) is
+// taken out of the row sum at the end.  11 VALU instructions per 8 codes,
+// then one FMA per code and token.
+//
+// Every size a buffer descriptor or a scalar offset is built from comes from
+// the host (F32Mat), so descriptors and row offsets stay in scalar registers.
+#include "common.h"
+#include "launch.h"
+#include "wl_wave.h"
+
+namespace qmoe {
+
+constexpr int F32_GU_ROWS = 32;     // gate (and up) rows per gate+up block
+constexpr int F32_DN_STEPS = 16;    // row steps per down wave
+constexpr int F32_U = 4;            // row steps per load batch
+constexpr int F32_MAX_WAVES = 8;
+
+// The pass of a block, in LDS: expert, token count and per token the row of
+// the pass's input (x: token; h: pair or sorted position), its token (the row
+// of out) and its routing weight.
+struct PassLds {
+    int e, nt;
+    int hrow[4], tok[4];
+    float w[4];
+};
+
+// Plan of slot a, computed by one wave into LDS (lane 0 writes).
+// inline: slot = pair a; it starts a pass when a's rank among its expert's
+//   pairs (ascending) is a multiple of TB, and the pass takes the next TB - 1
+//   pairs of that expert.  sid = the ids staged in LDS (n <= F32_INLINE_MAX).
+// record: plan record a over sorted positions (preparation kernel).
+// direct: expert 0, tokens a*TB ...
+template <int TB>
+__device__ void plan_wave(const F32Route &r, int a, const int *sid, PassLds *pl) {
+    const int lane = lane_id();
+    int e = -1, nt = 0;
+    int hrow[TB], tok[TB];
+    float w[TB];
+#pragma unroll
+    for (int j = 0; j < TB; j++) {
+        hrow[j] = 0;
+        tok[j] = 0;
+        w[j] = 0.f;
+    }
+    if (r.ids) {
+        if (a < r.n) {
+            const int e0 = sid[a];
+            if (e0 >= 0 && e0 < r.E) {
+                e = e0;
+                nt = 1;
+                hrow[0] = a;
+                int rank = 0;
+                if (TB > 1) {
+                    const int nc = (r.n + QMOE_WAVE - 1) / QMOE_WAVE;
+                    const int ca = a / QMOE_WAVE, la = a % QMOE_WAVE;
+                    for (int c = 0; c < nc; c++) {
+                        const int q = c * QMOE_WAVE + lane;
+                        const int v = q < r.n ? sid[q] : -1;
+                        uint64_t m = __ballot(v == e);
+                        if (c < ca) {
+                            rank += __popcll(m);
+                            continue;
+                        }
+                        if (c == ca) {
+                            rank += __popcll(m & ((1ull << la) - 1ull));
+                            m = la == 63 ? 0ull : (m & ~((2ull << la) - 1ull));
+                        }
+#pragma unroll
+                        for (int j = 1; j < TB; j++)
+                            if (nt == j && m) {
+                                hrow[j] = c * QMOE_WAVE + __builtin_ctzll(m);
+                                m &= m - 1ull;
+                                nt++;
+                            }
+                        if (nt == TB) break;
+                    }
+                    // a pair whose rank is not a multiple of TB belongs to an
+                    // earlier pass; the ranks of the pairs before a suffice
+                    // because the partners only come after a
+                    if (rank % TB) nt = 0;
+                }
+#pragma unroll
+                for (int j = 0; j < TB; j++)
+                    if (j < nt) {
+                        tok[j] = hrow[j] / r.k;
+                        w[j] = r.topk_w[hrow[j]];
+                    }
+            }
+        }
+    } else if (r.rec) {
+        if (a < r.max_rec) {
+            const u32x4 rc = *(const u32x4 *)(r.rec + 4 * a);
+            if ((int)rc.x >= 0) {
+                e = (int)rc.x;
+                nt = (int)rc.z - (int)rc.y;
+#pragma unroll
+                for (int j = 0; j < TB; j++)
+                    if (j < nt) {
+                        hrow[j] = (int)rc.y + j;
+                        tok[j] = r.tok[hrow[j]];
+                        w[j] = r.wsort[hrow[j]];
+                    }
+            }
+        }
+    } else {
+        const int t0 = a * TB;
+        if (t0 < r.ntok) {
+            e = 0;
+            nt = min(TB, r.ntok - t0);
+#pragma unroll
+            for (int j = 0; j < TB; j++) {
+                hrow[j] = t0 + (j < nt ? j : 0);
+                tok[j] = hrow[j];
+                w[j] = 1.f;
+            }
+        }
+    }
+    if (lane == 0) {
+        pl->e = e;
+        pl->nt = e < 0 ? 0 : nt;
+#pragma unroll
+        for (int j = 0; j < TB; j++) {
+            pl->hrow[j] = hrow[j];
+            pl->tok[j] = tok[j];
+            pl->w[j] = w[j];
+        }
+    }
+}
+
+// Stage the plan of this block into LDS (inline mode stages the ids first)
+// and return its token count (0: nothing to do; uniform over the block).
+template <int TB>
+__device__ __forceinline__ int stage_plan(const F32Route &r, int a, int *sid, PassLds *pl) {
+    if (r.ids) {
+        for (int i = threadIdx.x; i < r.n; i += blockDim.x) sid[i] = r.ids[i];
+        __syncthreads();
+    }
+    if (wave_id() == 0) plan_wave<TB>(r, a, sid, pl);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(pl->nt);
+}
+
+// Buffer descriptors of one expert's matrix and this lane's byte offsets
+// (its chunk's 16 packed bytes and its scale) inside a row.
+struct SliceSrc {
+    __amdgpu_buffer_rsrc_t q, s;
+    uint32_t qlane, slane;
+};
+
+__device__ __forceinline__ SliceSrc slice_src(const F32Mat &M, int e, int chunk) {
+    SliceSrc r;
+    r.q = make_rsrc(M.q + (int64_t)e * M.q_stride, M.qbytes);
+    r.s = make_rsrc(M.s + (int64_t)e * M.s_stride, M.sbytes);
+    const bool ok = chunk < M.chunks;
+    r.qlane = ok ? (uint32_t)chunk * 16u : OOB_OFFSET;
+    r.slane = ok ? (((uint32_t)chunk * 32u) >> M.gshift) * 4u : OOB_OFFSET;
+    return r;
+}
+
+// This lane's 32 activations of `row` (a row of `cols` f32 starting at
+// base + row * ld); zero for a chunk past the row.  `vec` = 16-byte loads.
+__device__ __forceinline__ void load_chunk(float (&x)[32], const float *base, int64_t row,
+                                           int64_t ld, int col0, int cols, bool vec) {
+    if (col0 >= cols) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) x[i] = 0.f;
+        return;
+    }
+    const float *p = base + row * ld + col0;
+    if (vec && col0 + 32 <= cols) {
+#pragma unroll
+        for (int v = 0; v < 8; v++) {
+            const f32x4 t = *(const f32x4 *)(p + 4 * v);
+            x[4 * v + 0] = t.x;
+            x[4 * v + 1] = t.y;
+            x[4 * v + 2] = t.z;
+            x[4 * v + 3] = t.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; i++) x[i] = col0 + i < cols ? p[i] : 0.f;
+    }
+}
+
+// acc[t] = sum over the chunk of (16 q_i) x[t][i]: the 32 codes of one 16-byte
+// load against NT tokens' activations.
+template <int TB, int NT>
+__device__ __forceinline__ void chunk_fma(const u32x4 &w, const float (&x)[TB][32],
+                                          float (&acc)[TB]) {
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        const uint32_t v = w[d];
+        const uint32_t hi = (v & 0xF0F0F0F0u) ^ 0x80808080u;
+        const uint32_t lo = ((v << 4) & 0xF0F0F0F0u) ^ 0x80808080u;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float fe = (float)(int8_t)(lo >> (8 * b));
+            const float fo = (float)(int8_t)(hi >> (8 * b));
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                acc[t] = fmaf(fe, x[t][8 * d + 2 * b], acc[t]);
+                acc[t] = fmaf(fo, x[t][8 * d + 2 * b + 1], acc[t]);
+            }
+        }
+    }
+}
+
+// Stream NST row steps of one slice: step j reads row row0 + j*(64/L) + the
+// lane's sub-row (the last row of the matrix past its end), in batches of
+// F32_U steps with the next batch's loads issued before the current batch is
+// computed.  The L-lane sum of step j, token t lands in
+// red[t * ld + j * (64/L) + sub-row].
+template <int L, int TB, int NT, int NST>
+__device__ __forceinline__ void stream_slice(const SliceSrc &src, uint32_t rb, uint32_t sb,
+                                             int row0, int rows, const float (&x)[TB][32],
+                                             float *red, int ld) {
+    constexpr int RPI = QMOE_WAVE / L;
+    constexpr int NB = NST / F32_U;
+    static_assert(NB * F32_U == NST, "steps must be a multiple of the batch");
+    const int lane = lane_id();
+    const int sr = lane / L;
+    u32x4 wq[2][F32_U];
+    float ws[2][F32_U];
+    auto load = [&](int b, int slot) {
+#pragma unroll
+        for (int u = 0; u < F32_U; u++) {
+            const int j = b * F32_U + u;
+            if (RPI == 1) {
+                // one row per wave instruction: the row offset is scalar
+                const int row = min(row0 + j, rows - 1);
+                wq[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane,
+                                                                    (uint32_t)row * rb, 0);
+                ws[slot][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    src.s, src.slane, (uint32_t)row * sb, 0));
+            } else {
+                const int row = min(row0 + j * RPI + sr, rows - 1);
+                wq[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(
+                    src.q, src.qlane + (uint32_t)row * rb, 0u, 0);
+                ws[slot][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    src.s, src.slane + (uint32_t)row * sb, 0u, 0));
+            }
+        }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+        if (b + 1 < NB) load(b + 1, (b + 1) & 1);
+#pragma unroll
+        for (int u = 0; u < F32_U; u++) {
+            float acc[TB];
+            chunk_fma<TB, NT>(wq[b & 1][u], x, acc);
+#pragma unroll
+            for (int t = 0; t < NT; t++) {
+                const float v = reduce_dpp<L>(acc[t] * ws[b & 1][u]);
+                if ((lane % L) == L - 1) red[t * ld + (b * F32_U + u) * RPI + sr] = v;
+            }
+        }
+    }
+}
+
+// The NT-token instance of a slice stream, chosen by the pass's token count.
+template <int L, int TB, int NST>
+__device__ __forceinline__ void stream_slice_nt(int nt, const SliceSrc &src, uint32_t rb,
+                                                uint32_t sb, int row0, int rows,
+                                                const float (&x)[TB][32], float *red, int ld) {
+    if (TB >= 4 && nt == 4)
+        stream_slice<L, TB, (TB >= 4 ? 4 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+    else if (TB >= 3 && nt == 3)
+        stream_slice<L, TB, (TB >= 3 ? 3 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+    else if (TB >= 2 && nt == 2)
+        stream_slice<L, TB, (TB >= 2 ? 2 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+    else
+        stream_slice<L, TB, 1, NST>(src, rb, sb, row0, rows, x, red, ld);
+}
+
+// Blocks per SIMD the register allocation targets, per tokens per pass (no
+// instance spills at these targets).
+template <int TB>
+constexpr int f32_waves_per_eu() { return TB == 1 ? 4 : 2; }
+
+// Slot index of this block (grid y and z together).
+__device__ __forceinline__ int f32_slot() { return blockIdx.z * gridDim.y + blockIdx.y; }
+
+// Leading row of an inline gate+up launch: the worklist view of the call
+// (block 0, one wave) and out <- 0 for the down projection's atomic adds.
+__device__ void f32_lead_row(const F32Route &r, int *lds) {
+    const int64_t total = (int64_t)r.out_tokens * r.out_cols;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
+        r.out[i] = 0.f;
+    if (blockIdx.x == 0 && wave_id() == 0) {
+        DecodePlan none{};
+        wl_wave(r.ids, r.topk_w, r.n, r.k, r.E, r.wl, none, lds, lds + (r.E + 1));
+    }
+}
+
+// LDS of a block: the cross-slice sums (nred floats), the pass, the staged ids.
+struct F32Lds {
+    float *red;
+    PassLds *pl;
+    int *sid;
+};
+__device__ __forceinline__ F32Lds f32_lds(float *base, int nred) {
+    F32Lds l;
+    l.red = base;
+    l.pl = reinterpret_cast<PassLds *>(base + nred);
+    l.sid = reinterpret_cast<int *>(base + nred) + sizeof(PassLds) / sizeof(int);
+    return l;
+}
+
+// ---------------------------------------------------------------------------
+// gate+up: block = (32 rows of F, one pass).  Waves 0..S-1 stream the gate
+// slices, waves S..2S-1 the same rows of up; the epilogue writes
+// h = silu(g) * u in f32 for the pass's tokens, row hrow of h.
+// ---------------------------------------------------------------------------
+template <int L, int TB>
+__global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
+    __attribute__((amdgpu_waves_per_eu(f32_waves_per_eu<TB>())))
+    f32_gateup_kernel(F32Mat G, F32Mat Up, const float *__restrict__ x, float *__restrict__ h,
+                      F32Route r, int S) {
+    extern __shared__ float lds_gu[];
+    constexpr int RPI = QMOE_WAVE / L;
+    constexpr int NST = F32_GU_ROWS / RPI;
+    int a = f32_slot();
+    if (r.lead_row) {
+        if (a == 0) {
+            f32_lead_row(r, (int *)lds_gu);
+            return;
+        }
+        a -= 1;
+    }
+    const int nred = 2 * S * TB * F32_GU_ROWS;
+    const F32Lds l = f32_lds(lds_gu, nred);
+    const int nt = stage_plan<TB>(r, a, l.sid, l.pl);
+    if (nt == 0) return;
+    const int e = __builtin_amdgcn_readfirstlane(l.pl->e);
+    const int H = G.cols, F = G.rows;
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int m = w / S, s = w % S;
+    const int chunk = s * L + lane_id() % L;
+    const F32Mat &M = m ? Up : G;
+    const SliceSrc src = slice_src(M, e, chunk);
+    float xr[TB][32];
+#pragma unroll
+    for (int t = 0; t < TB; t++)
+        if (t < nt) load_chunk(xr[t], x, l.pl->tok[t], H, chunk * 32, H, true);
+    const int row0 = blockIdx.x * F32_GU_ROWS;
+    float *red = l.red + (m * S + s) * TB * F32_GU_ROWS;
+    stream_slice_nt<L, TB, NST>(nt, src, M.rb, M.sb, row0, F, xr, red, F32_GU_ROWS);
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < nt * F32_GU_ROWS) {
+        const int t = tid / F32_GU_ROWS, rr = tid % F32_GU_ROWS;
+        const int f = row0 + rr;
+        if (f < F) {
+            float g = 0.f, u = 0.f;
+            for (int k = 0; k < S; k++) {
+                g += l.red[(k * TB + t) * F32_GU_ROWS + rr];
+                u += l.red[((S + k) * TB + t) * F32_GU_ROWS + rr];
+            }
+            g *= 0.0625f;
+            u *= 0.0625f;
+            h[(int64_t)l.pl->hrow[t] * F + f] = silu(g) * u;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down (and the plain matvec): block = (R * 16 * 64/L output rows, one pass);
+// wave w streams slice w % S of row group w / S.  Routed: out[tok] += w * y
+// with f32 atomics (out was cleared ahead of the launch); direct: out = y.
+// ---------------------------------------------------------------------------
+template <int L, int TB>
+__global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
+    __attribute__((amdgpu_waves_per_eu(f32_waves_per_eu<TB>())))
+    f32_down_kernel(F32Mat D, const float *__restrict__ hin, int64_t h_ld, int h_cols,
+                    float *__restrict__ out, F32Route r, int S, int R, bool routed, bool vec) {
+    extern __shared__ float lds_dn[];
+    constexpr int RPI = QMOE_WAVE / L;
+    constexpr int RW = F32_DN_STEPS * RPI;     // rows per row group
+    const int NR = R * RW;
+    const F32Lds l = f32_lds(lds_dn, S * TB * NR);
+    const int nt = stage_plan<TB>(r, f32_slot(), l.sid, l.pl);
+    if (nt == 0) return;
+    const int e = __builtin_amdgcn_readfirstlane(l.pl->e);
+    const int O = D.rows;
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int s = w % S, rg = w / S;
+    const int chunk = s * L + lane_id() % L;
+    const SliceSrc src = slice_src(D, e, chunk);
+    float xr[TB][32];
+#pragma unroll
+    for (int t = 0; t < TB; t++)
+        if (t < nt) load_chunk(xr[t], hin, l.pl->hrow[t], h_ld, chunk * 32, h_cols, vec);
+    const int row0 = blockIdx.x * NR;
+    float *red = l.red + s * TB * NR + rg * RW;
+    stream_slice_nt<L, TB, F32_DN_STEPS>(nt, src, D.rb, D.sb, row0 + rg * RW, O, xr, red, NR);
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * NR; i += blockDim.x) {
+        const int t = i / NR, rr = i % NR;
+        const int o = row0 + rr;
+        if (o >= O) continue;
+        float y = 0.f;
+        for (int k = 0; k < S; k++) y += l.red[(k * TB + t) * NR + rr];
+        y *= 0.0625f;
+        float *dst = out + (int64_t)l.pl->tok[t] * O + o;
+        if (routed) unsafeAtomicAdd(dst, l.pl->w[t] * y);
+        else *dst = y;
+    }
+}
+
+// Lane layout for rows of `cols` inputs: L lanes per slice, S slices, at most
+// smax slices; fewest idle lanes, then widest L.  {0, 0} if none fits.
+struct F32Shape {
+    int L, S;
+};
+static F32Shape f32_shape(int cols, int smax) {
+    const int C = cols / 32;
+    F32Shape best{0, 0};
+    int best_waste = 1 << 30;
+    const int Ls[3] = {64, 32, 16};
+    for (int i = 0; i < 3; i++) {
+        const int L = Ls[i];
+        const int S = (C + L - 1) / L;
+        if (S > smax) continue;
+        const int waste = S * L - C;
+        if (waste < best_waste) {
+            best_waste = waste;
+            best = F32Shape{L, S};
+        }
+    }
+    return best;
+}
+
+bool f32_gateup_supported(int hidden) {
+    return hidden % 64 == 0 && f32_shape(hidden, F32_MAX_WAVES / 2).L != 0;
+}
+bool f32_down_supported(int cols) {
+    return cols % 64 == 0 && f32_shape(cols, F32_MAX_WAVES).L != 0;
+}
+
+// The uniform sizes of a matrix the kernels use (no division on the device).
+F32Mat f32_mat(const QMat &m) {
+    F32Mat f;
+    f.q = m.q;
+    f.s = m.s;
+    f.q_stride = m.q_stride;
+    f.s_stride = m.s_stride;
+    f.rows = m.rows;
+    f.cols = m.cols;
+    f.chunks = m.cols / 32;
+    f.rb = (uint32_t)(m.cols / 2);
+    f.sb = (uint32_t)scales_per_row(m) * 4u;
+    f.qbytes = (int64_t)m.rows * f.rb;
+    f.sbytes = (int64_t)m.rows * f.sb;
+    if (m.group >= m.cols) {
+        f.gshift = 31;                 // one scale per row: index 0
+    } else {
+        int j = 0;
+        while ((1 << j) < m.group) j++;
+        f.gshift = j;                  // group 32 or 64 * 2^i: a power of two
+    }
+    return f;
+}
+
+// Tokens per weight pass (a pass shares one read of the weights among its
+// tokens; more tokens per pass cost registers and occupancy).
+int f32_tokens_per_pass(int pairs, int experts, bool gateup) {
+    (void)gateup;
+    if (pairs >= 4 * (int64_t)experts) return 4;
+    if (pairs > 1 && 2 * (int64_t)pairs >= experts) return 2;
+    return 1;
+}
+
+static dim3 f32_grid(unsigned x, int64_t slots) {
+    const int64_t gy = slots < 65535 ? (slots > 0 ? slots : 1) : 65535;
+    return dim3(x, (unsigned)gy, (unsigned)((slots + gy - 1) / gy));
+}
+
+// Grid slots of a launch: inline = one per pair (+ the leading row), record =
+// max_rec, direct = ceil(ntok / tb).
+static int64_t f32_slots(const F32Route &r, int tb) {
+    if (r.ids) return (int64_t)r.n + (r.lead_row ? 1 : 0);
+    if (r.rec) return r.max_rec;
+    return (r.ntok + tb - 1) / tb;
+}
+
+// Dynamic LDS of a launch: the cross-slice sums, the pass and (inline) the
+// staged ids; a leading row needs the one-wave worklist's two counters of
+// E + 1 ints.
+static size_t f32_lds_bytes(const F32Route &r, size_t nred) {
+    size_t b = nred * sizeof(float) + sizeof(PassLds) + (r.ids ? (size_t)r.n * sizeof(int) : 0);
+    if (r.ids && r.lead_row) {
+        const size_t wl = (size_t)2 * (r.E + 1) * sizeof(int);
+        b = b > wl ? b : wl;
+    }
+    return b;
+}
+
+hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, float *h,
+                             const F32Route &r, int tb, hipStream_t st) {
+    const F32Shape sh = f32_shape(gate.cols, F32_MAX_WAVES / 2);
+    if (!sh.L || (r.ids && r.n > F32_INLINE_MAX)) return hipErrorInvalidValue;
+    const dim3 grid = f32_grid((gate.rows + F32_GU_ROWS - 1) / F32_GU_ROWS, f32_slots(r, tb));
+    const dim3 block(2 * sh.S * QMOE_WAVE);
+    const size_t lds = f32_lds_bytes(r, (size_t)2 * sh.S * tb * F32_GU_ROWS);
+    const F32Mat G = f32_mat(gate), U = f32_mat(up);
+#define X(L_, T_)                                                                              \
+    if (sh.L == L_ && tb == T_) {                                                              \
+        hipLaunchKernelGGL((f32_gateup_kernel<L_, T_>), grid, block, lds, st, G, U, x, h, r,   \
+                           sh.S);                                                              \
+        return hipGetLastError();                                                              \
+    }
+    X(64, 1) X(64, 2) X(64, 4) X(32, 1) X(32, 2) X(32, 4) X(16, 1) X(16, 2) X(16, 4)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int h_cols,
+                           float *out, const F32Route &r, int tb, bool routed, hipStream_t st) {
+    const F32Shape sh = f32_shape(down.cols, F32_MAX_WAVES);
+    if (!sh.L || (r.ids && r.n > F32_INLINE_MAX) || r.lead_row) return hipErrorInvalidValue;
+    int R = 4 / sh.S;
+    if (R < 1) R = 1;
+    const int NR = R * F32_DN_STEPS * (QMOE_WAVE / sh.L);
+    const dim3 grid = f32_grid((down.rows + NR - 1) / NR, f32_slots(r, tb));
+    const dim3 block(sh.S * R * QMOE_WAVE);
+    const size_t lds = f32_lds_bytes(r, (size_t)sh.S * tb * NR);
+    const bool vec = h_cols % 4 == 0 && h_ld % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(hin) & 15u) == 0;
+    const F32Mat D = f32_mat(down);
+#define X(L_, T_)                                                                              \
+    if (sh.L == L_ && tb == T_) {                                                              \
+        hipLaunchKernelGGL((f32_down_kernel<L_, T_>), grid, block, lds, st, D, hin, h_ld,       \
+                           h_cols, out, r, sh.S, R, routed, vec);                              \
+        return hipGetLastError();                                                              \
+    }
+    X(64, 1) X(64, 2) X(64, 4) X(32, 1) X(32, 2) X(32, 4) X(16, 1) X(16, 2) X(16, 4)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qmoe

@@ -124,6 +124,51 @@ int gemv_tokens_per_pass(const QMat &m, int pairs, int experts, bool gateup);
 hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
                               hipStream_t st);
 
+// Decode GEMVs in f32 arithmetic.  Each launch block handles one weight pass
+// (one expert, up to tb tokens) found from its grid slot in one of three
+// modes: inline (ids set: slot = pair, the pass grouping derived in every
+// block from the ids, for at most F32_INLINE_MAX pairs), record (rec set:
+// plan records over sorted positions from the preparation kernel) or direct
+// (neither: expert 0, slot a = tokens a*tb ..).  The rows of h are pairs
+// (inline), sorted positions (record) or tokens (direct).
+constexpr int F32_INLINE_MAX = 1024;
+struct F32Route {
+    const int32_t *ids;     // inline: topk ids [n]
+    const float *topk_w;    // inline: routing weights [n]
+    int n, k, E;
+    const int32_t *rec;     // record: plan records (see DecodePlan)
+    const int32_t *tok;     // record: token of each sorted position
+    const float *wsort;     // record: weight of each sorted position
+    int max_rec;
+    int ntok;               // direct: tokens
+    int lead_row;           // inline gate+up: grid row 0 writes the worklist view and clears out
+    Worklist wl;            // lead row: worklist view arrays
+    float *out;             // lead row: output to clear
+    int out_tokens, out_cols;
+};
+// A matrix stack as the f32 kernels see it: every size a buffer descriptor
+// or a row offset is built from is computed on the host.
+struct F32Mat {
+    const uint8_t *q;
+    const float *s;
+    int64_t q_stride, s_stride;   // bytes / floats between experts
+    int64_t qbytes, sbytes;       // one expert's codes and scales, in bytes
+    int rows, cols, chunks;       // chunks = cols / 32
+    uint32_t rb, sb;              // bytes per row of codes and of scales
+    int gshift;                   // scale index of input i: i >> gshift (31: one per row)
+};
+F32Mat f32_mat(const QMat &m);
+bool f32_gateup_supported(int hidden);
+bool f32_down_supported(int cols);
+int f32_tokens_per_pass(int pairs, int experts, bool gateup);
+// h[hrow][F] = silu(G x) * (U x) in f32 (x f32 [tokens][H]).
+hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, float *h,
+                             const F32Route &r, int tb, hipStream_t st);
+// y = D h over rows of h (h_ld floats apart, h_cols valid inputs, zero past
+// them); routed: out[tok] += w * y (atomics), else out[tok] = y.
+hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int h_cols,
+                           float *out, const F32Route &r, int tb, bool routed, hipStream_t st);
+
 // Prefill (bf16 activations, MFMA).
 constexpr int MFMA_BM = 256;
 struct MfmaRoute {

@@ -42,7 +42,8 @@ extern "C" int qmoe_layer_noalloc(const qmoe_layer_desc *desc, int32_t x_dtype, 
     if (!desc) return QMOE_ERR_NULL;
     if (desc->struct_size != sizeof(qmoe_layer_desc)) return QMOE_ERR_ABI;
     if (tokens < 0 || k < 1) return QMOE_ERR_SHAPE;
-    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16) return QMOE_ERR_UNSUPPORTED;
+    if (x_dtype != QMOE_F32 && x_dtype != QMOE_BF16 && x_dtype != QMOE_F32_DIGITS)
+        return QMOE_ERR_UNSUPPORTED;
     const size_t need = qmoe_layer_workspace_bytes(desc, tokens, k, x_dtype);
     if (need > (size_t)QMOE_NOALLOC_SCRATCH_BYTES) return QMOE_ERR_SCRATCH;
     int dev = 0;

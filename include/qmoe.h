@@ -74,12 +74,29 @@ enum {
     QMOE_ERR_SCRATCH = 9      /* more than qmoe_layer_noalloc's fixed scratch */
 };
 
-/* Activation dtypes.  The dtype of x selects the path: f32 = decode (GEMV
- * kernels), bf16 = prefill (grouped MFMA kernels).  The bf16 path feeds the
- * matrix cores f16 operands: q * s and the gated intermediate h must stay in
- * the f16 range (|s| < 8188, |h| < 65504), larger values giving inf; the
- * accumulators and every output are f32. */
-enum { QMOE_F32 = 0, QMOE_BF16 = 1 };
+/* Activation dtypes.  The dtype of x selects the path:
+ *  - QMOE_F32: decode path in f32 arithmetic (GEMV kernels): every int4 code
+ *    is unpacked to an exact f32, multiplied with the f32 activation and
+ *    accumulated in f32 per 64-input group, the group's f32 scale applied
+ *    once per group (the grouped kernel of the colibri pull request, comment
+ *    "blocked by GPU driver instability"); h = silu(g) * u is kept in f32.
+ *    Widths: hidden <= 8192 into gate/up, inter <= 16384 into down.
+ *  - QMOE_F32_DIGITS: x is also f32 [tokens][H], but the activations are
+ *    rounded to 18-bit block fixed point (one power-of-two exponent per
+ *    64-element group of x and per 32-element chunk of h) and multiplied
+ *    with the codes in integer dot products; an element far below its
+ *    group's largest keeps fewer bits (error up to 2^(E-19) per element,
+ *    2^(E-1) <= the group's max |x| < 2^E).  A faster variant that has to be
+ *    asked for; widths: a multiple of 64 up to 12288.
+ *  - QMOE_BF16: prefill path (grouped MFMA kernels).  The matrix cores take
+ *    f16 operands: q * s is rounded to f16 (|s| < 8188; scales below 2^-14
+ *    become f16 subnormals and lose relative precision, below about 2^-16
+ *    the rounding alone approaches the 2e-3 bar), and the gated
+ *    intermediate h is stored as f16 (|h| < 65504, larger values giving
+ *    inf); the accumulators and every output are f32.
+ * A NaN or infinity in x reaches every output it feeds on the f32 and bf16
+ * paths. */
+enum { QMOE_F32 = 0, QMOE_BF16 = 1, QMOE_F32_DIGITS = 2 };
 
 /* One grouped int4 matrix, or a stack of per-expert matrices of one shape.
  * q_expert_stride is the byte distance between experts' packed codes and
@@ -275,10 +292,16 @@ size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
  * and must not overlap x, the routing arrays or the workspace.  Routing is
  * an input: the layer does not pick experts.  Ids outside [0, E) are
  * dropped.  After the call the workspace begins with the worklist in the
- * layout of qmoe_layer_ws_view (for inspection and tests).  On the decode
- * path an expert's tokens are taken one or two per weight pass; the passes
- * of one expert run side by side, so its weights come from HBM about once
- * per call and the later passes read them from the L2 cache. */
+ * layout of qmoe_layer_ws_view (for inspection and tests).  On the f32
+ * paths an expert's tokens are taken one, two or four per weight pass; the
+ * passes of one expert run side by side, so its weights come from HBM about
+ * once per call and the later passes read them from the L2 cache.  With
+ * QMOE_F32 and at most 1024 pairs (tokens * k) the call is two kernel
+ * launches (gate+up, which also groups the pairs by expert, then down).
+ * Reproducibility: the bf16 path sums each token's k expert rows in pick
+ * order and gives bit-identical results from run to run; the f32 paths add
+ * the k expert terms into out with f32 atomics, so their order, and the
+ * last bits of out, may differ from run to run. */
 int qmoe_layer(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x,
                int32_t tokens, const int32_t *topk_ids, const float *topk_w,
                int32_t k, float *out, void *ws, size_t ws_bytes, void *stream);
@@ -299,9 +322,12 @@ int qmoe_layer_logits(const qmoe_layer_desc *desc, int32_t x_dtype, const void *
 /* qmoe_layer with phase markers: when phase_events is non-NULL it holds
  * n_events hipEvent_t handles (passed as void*, created by the caller) and the
  * call records events[0] before its first kernel and events[i] after phase i
- * on `stream`.  Phases: f32 path 1 = worklist + activation digits, 2 = gate+up,
- * 3 = down + combine (n_events >= 4); bf16 path 1 = worklist + activation
- * prep, 2 = gate+up, 3 = down, 4 = combine (n_events >= 5).  Fewer events = QMOE_ERR_SHAPE.
+ * on `stream`.  Phases: f32 paths 1 = worklist (+ activation digits for
+ * QMOE_F32_DIGITS; for QMOE_F32 with at most 1024 pairs the gate+up launch
+ * builds the worklist itself and phase 1 is empty), 2 = gate+up, 3 = down and
+ * combine (n_events >= 4); bf16 path 1 = worklist + activation prep,
+ * 2 = gate+up, 3 = down, 4 = combine (n_events >= 5).  Fewer events =
+ * QMOE_ERR_SHAPE.
  * Recording an event allocates nothing and does not synchronise.  This is
  * the per-launch event timing the maintainer asks for in the pull request
  * (data request: elapsed time around one launch per shape). */

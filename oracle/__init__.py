@@ -13,7 +13,9 @@ are exact in double), so the oracle sees the same numbers the GPU sees.
 Parity status of each function (what pins it is in ``tests/test_oracle_*``):
 pack/unpack, import_twos, detect_group, matvec, pair, silu, ffn, worklist,
 layer and route are all pinned by hand-written values, closed forms or brute
-force; none is "parity unpinned".
+force; dsilu, matvec_abs and layer_mag (the scales of the per-element error
+check) by closed forms and by perturbing a separate float64 evaluation of
+the layer; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -85,6 +87,13 @@ def load(path=None):
     lib.orc_import_twos.argtypes = [vp, i64, i64, vp]
     lib.orc_detect_group.restype = i64
     lib.orc_detect_group.argtypes = [i64, i64, i64]
+    lib.orc_dsilu.restype = ctypes.c_double
+    lib.orc_dsilu.argtypes = [ctypes.c_double]
+    lib.orc_matvec_abs.restype = None
+    lib.orc_matvec_abs.argtypes = [vp, vp, i64, i64, i64, vp, i64, vp]
+    lib.orc_layer_mag.restype = None
+    lib.orc_layer_mag.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp,
+                                  i64, vp, vp, i64, vp]
     if path is None:
         _lib = lib
     return lib
@@ -217,6 +226,36 @@ class Oracle:
                                  _p(sd), experts, hidden, inter, gs, _p(x),
                                  tokens, _p(ids), _p(w), k, _p(out))
         return out, int(bad)
+
+    def dsilu(self, z):
+        return float(self.lib.orc_dsilu(float(z)))
+
+    def matvec_abs(self, packed, scales, cols, x, gs=64):
+        """A[b, o] = sum_i |deq(W)[o, i] x[b, i]| (per-element error scale)."""
+        packed = _c(_np(packed), np.uint8)
+        scales = _c(_np(scales), np.float32)
+        x = _c(_np(x), np.float64)
+        rows = packed.shape[0]
+        xb = x.reshape(-1, cols)
+        a = np.empty((xb.shape[0], rows), dtype=np.float64)
+        self.lib.orc_matvec_abs(_p(packed), _p(scales), rows, cols, gs, _p(xb),
+                                xb.shape[0], _p(a))
+        return a
+
+    def layer_mag(self, pg, sg, pu, su, pd, sd, hidden, inter, x, ids, w, gs=64):
+        """M[t, o]: first-order change of out[t, o] under a unit relative error
+        of every gate/up product, every h and every down product."""
+        pg, pu, pd = (_c(_np(a), np.uint8) for a in (pg, pu, pd))
+        sg, su, sd = (_c(_np(a), np.float32) for a in (sg, su, sd))
+        experts = pg.shape[0]
+        x = _c(_np(x), np.float64).reshape(-1, hidden)
+        ids = _c(_np(ids), np.int32)
+        w = _c(_np(w), np.float32)
+        tokens, k = ids.shape
+        mag = np.empty((tokens, hidden), dtype=np.float64)
+        self.lib.orc_layer_mag(_p(pg), _p(sg), _p(pu), _p(su), _p(pd), _p(sd), experts,
+                               hidden, inter, gs, _p(x), tokens, _p(ids), _p(w), k, _p(mag))
+        return mag
 
     def route(self, logits, k):
         """Top-k ids (pick order) and f32 softmax weights over the picked."""

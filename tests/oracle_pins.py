@@ -540,4 +540,102 @@ def pin_detect_group_brute(orc):
             assert all(rows * (-(-cols // c)) * 4 != nbytes for c in cands if c < got)
 
 
+# ------------------------------------------- per-element error scales ---
+# The maintainer comment "Here's the oracle you're missing": a float result is
+# judged against the sum of the magnitudes of its terms.
+
+def pin_dsilu_values(orc):
+    """silu'(0) = 1/2, silu' -> 1 and 0 at the far ends, silu' = 0 at the
+    minimum of silu (z = -1.2784645427610738), and a central difference of the
+    oracle's own silu elsewhere."""
+    assert orc.dsilu(0.0) == 0.5
+    assert abs(orc.dsilu(40.0) - 1.0) <= 1e-15
+    assert abs(orc.dsilu(-40.0)) <= 1e-15
+    assert abs(orc.dsilu(-1.2784645427610738)) <= 1e-15
+    for z in (-3.0, -0.7, 0.3, 1.0, 2.5):
+        h = 1e-5
+        fd = (orc.silu(z + h) - orc.silu(z - h)) / (2 * h)
+        assert abs(orc.dsilu(z) - fd) <= 1e-9, z
+
+
+def pin_matvec_abs_library(orc):
+    """A = |deq(W)| @ |x| (numpy dense); equals y when every term is >= 0;
+    never below |y|."""
+    rng = _rng(40)
+    O, I = 19, 200
+    q = rng.integers(-8, 8, size=(O, I), dtype=np.int8)
+    s = rng.uniform(0.005, 0.02, size=(O, -(-I // 64))).astype(np.float32)
+    x = rng.standard_normal((3, I))
+    packed, _ = orc.pack(q)
+    a = orc.matvec_abs(packed, s, I, x)
+    W = q.astype(np.float64) * s.astype(np.float64)[:, np.arange(I) // 64]
+    _close(a, np.abs(x) @ np.abs(W).T, 1e-13, 0, "abs")
+    assert np.all(a >= np.abs(orc.matvec(packed, s, I, x)) * (1 - 1e-15))
+    qp = np.abs(q).astype(np.int8) % 8
+    pp, _ = orc.pack(qp)
+    xp = np.abs(x)
+    _close(orc.matvec_abs(pp, s, I, xp), orc.matvec(pp, s, I, xp), 1e-15, 0, "nonneg")
+
+
+def _layer_sensitivity(L, x, ids, w, t, o, H, F):
+    """Sum over all gate/up products, h values and down products of
+    |d out[t, o] / d(relative error of that quantity)|, by float64 autograd of
+    a dense evaluation of the layer (independent of the oracle's C code)."""
+    import torch
+
+    def deq(q, s):
+        q = torch.as_tensor(q.astype(np.float64))
+        s = torch.as_tensor(s.astype(np.float64))
+        return q * s[:, torch.arange(q.shape[1]) // 64]
+    xt = torch.as_tensor(x[t], dtype=torch.float64)
+    total = 0.0
+    for j in range(ids.shape[1]):
+        e = int(ids[t, j])
+        G, U, D = deq(L["qg"][e], L["sg"][e]), deq(L["qu"][e], L["su"][e]), deq(L["qd"][e], L["sd"][e])
+        fg = torch.ones(F, H, dtype=torch.float64, requires_grad=True)
+        fu = torch.ones(F, H, dtype=torch.float64, requires_grad=True)
+        fh = torch.ones(F, dtype=torch.float64, requires_grad=True)
+        fd = torch.ones(F, dtype=torch.float64, requires_grad=True)
+        g = (G * xt * fg).sum(1)
+        u = (U * xt * fu).sum(1)
+        h = g * torch.sigmoid(g) * u * fh
+        y = (D[o] * h * fd).sum()
+        out = float(w[t, j]) * y
+        out.backward()
+        total += sum(float(v.grad.abs().sum()) for v in (fg, fu, fh, fd))
+    return total
+
+
+def pin_layer_mag_autograd(orc):
+    """layer_mag[t, o] = the first-order sensitivity of out[t, o] to unit
+    relative errors of all its rounded quantities (float64 autograd)."""
+    rng = _rng(41)
+    E, H, F, T, K = 3, 128, 64, 2, 2
+    L = _rand_layer(orc, rng, E, H, F)
+    x = rng.standard_normal((T, H))
+    ids = np.array([[2, 0], [1, 2]], np.int32)
+    w = np.array([[0.7, -0.3], [0.55, 0.45]], np.float32)     # any sign is accepted
+    mag = orc.layer_mag(L["pg"], L["sg"], L["pu"], L["su"], L["pd"], L["sd"], H, F, x, ids, w)
+    for t, o in ((0, 0), (0, 77), (1, 5), (1, 127)):
+        ref = _layer_sensitivity(L, x, ids, w, t, o, H, F)
+        assert abs(mag[t, o] - ref) <= 1e-10 * ref, (t, o, mag[t, o], ref)
+    out, _ = orc.layer(L["pg"], L["sg"], L["pu"], L["su"], L["pd"], L["sd"], H, F, x, ids, w)
+    assert np.all(mag >= np.abs(out))
+
+
+def pin_layer_mag_dropped_ids(orc):
+    """Dropped ids add nothing; a token with only dropped ids has M = 0."""
+    rng = _rng(42)
+    E, H, F = 2, 64, 64
+    L = _rand_layer(orc, rng, E, H, F)
+    x = rng.standard_normal((2, H))
+    ids = np.array([[1, -1], [5, -3]], np.int32)
+    w = np.ones((2, 2), np.float32)
+    mag = orc.layer_mag(L["pg"], L["sg"], L["pu"], L["su"], L["pd"], L["sd"], H, F, x, ids, w)
+    one = orc.layer_mag(L["pg"], L["sg"], L["pu"], L["su"], L["pd"], L["sd"], H, F, x[:1],
+                        ids[:1, :1], w[:1, :1])
+    assert np.array_equal(mag[0], one[0])
+    assert np.all(mag[1] == 0.0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

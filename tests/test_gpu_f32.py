@@ -1,0 +1,169 @@
+"""The f32 decode path (QMOE_F32: every code unpacked to f32, f32 FMA chains,
+f32 group scale) and its digit variant (QMOE_F32_DIGITS), against the oracle:
+activations whose 64-element groups span a large dynamic range, NaN and
+infinity in x, the pass grouping of the two-launch call at and past its
+1024-pair limit, and the digit variant selected explicitly."""
+import numpy as np
+import pytest
+import torch
+
+import grouped_int4_expert_amd as qm
+import synth
+from gpu_util import F32_TOL, Layer, check, orc, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qm.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _outlier_x(g, rows, cols, ratio=1e4):
+    """Every 64-element group holds one element `ratio` times the scale of
+    the others (which are N(0,1) * 1e-3), at a random place and sign."""
+    x = synth.rand_x(g, (rows, cols)) * 1e-3
+    ng = cols // 64
+    pos = torch.randint(0, 64, (rows, ng), generator=g)
+    sign = torch.randint(0, 2, (rows, ng), generator=g).float() * 2 - 1
+    idx = torch.arange(ng) * 64 + pos
+    x.scatter_(1, idx, sign * 1e-3 * ratio)
+    return x
+
+
+def test_matvec_outlier_groups():
+    say("matvec 512x4096, one element per group 1e4x the rest")
+    g = synth.generator(501)
+    q = synth.rand_q(g, (512, 4096))
+    s = synth.rand_scales(g, (512, 64))
+    x = _outlier_x(g, 3, 4096)
+    y = qm.qmoe_matvec(qm.qmoe_pack(q.to(DEV)), s.to(DEV), 4096, x.to(DEV)).cpu().numpy()
+    pq, _ = orc().pack(q.numpy())
+    ref = orc().matvec(pq, s.numpy(), 4096, x.numpy())
+    mag = orc().matvec_abs(pq, s.numpy(), 4096, x.numpy())
+    err, worst = check(y, ref, mag, "f32", "matvec outliers")
+    assert err <= 1e-6
+
+
+def test_layer_outlier_groups_f32_and_digits():
+    """The f32 path keeps f32 accuracy on groups with a 1e4 dynamic range;
+    the digit variant rounds each group to 18 bits of its largest element,
+    so its small elements keep few bits and its error is far larger."""
+    say("layer E=16 H=1024 F=512 T=12 k=4, outlier groups")
+    L = Layer(16, 1024, 512, seed=502)
+    g = synth.generator(503)
+    x = _outlier_x(g, 12, 1024)
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, 12, 16), 4)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), w.to(DEV)
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    out = qm.qmoe_layer(L.dev, xd, idd, wd).cpu().numpy()
+    err_f32, _ = check(out, ref, mag, "f32", "f32 path")
+    dig = qm.qmoe_layer(L.dev, xd, idd, wd, x_dtype=qm.QMOE_F32_DIGITS).cpu().numpy()
+    err_dig = rel_l2(dig, ref)
+    say(f"  digit variant rel_l2 = {err_dig:.3e} (f32 path {err_f32:.3e})")
+    assert err_f32 <= 1e-6
+    assert err_dig > 10 * err_f32
+
+
+def test_matvec_nan_and_inf():
+    say("matvec NaN / inf in x")
+    g = synth.generator(504)
+    q = synth.rand_q(g, (96, 256))
+    s = synth.rand_scales(g, (96, 4))
+    x = synth.rand_x(g, (4, 256))
+    x[1, 5] = float("nan")
+    x[2, 200] = float("inf")
+    x[3, 17] = -float("inf")
+    y = qm.qmoe_matvec(qm.qmoe_pack(q.to(DEV)), s.to(DEV), 256, x.to(DEV)).cpu().numpy()
+    pq, _ = orc().pack(q.numpy())
+    ref = orc().matvec(pq, s.numpy(), 256, x.numpy())
+    assert np.isnan(ref[1]).all() and not np.isfinite(ref[2]).any()
+    check(y, ref, None, "f32", "matvec nan/inf")
+
+
+@pytest.mark.parametrize("code", [qm.QMOE_F32, qm.QMOE_F32_DIGITS, qm.QMOE_BF16])
+def test_layer_nan_reaches_its_token_only(code):
+    say(f"layer NaN in one token, path {code}")
+    L = Layer(8, 256, 128, seed=505)
+    g = synth.generator(506)
+    x = synth.rand_x(g, (9, 256))
+    x[4, 77] = float("nan")
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, 9, 8), 2)
+    xx = x.to(torch.bfloat16) if code == qm.QMOE_BF16 else x
+    out = qm.qmoe_layer(L.dev, xx.to(DEV), ids.to(DEV), w.to(DEV), x_dtype=code).cpu().numpy()
+    ref = L.oracle_layer(xx, ids, w)
+    assert np.isnan(ref[4]).all()
+    assert np.isnan(out[4]).all()
+    keep = [t for t in range(9) if t != 4]
+    assert np.isfinite(out[keep]).all()
+    path = "bf16" if code == qm.QMOE_BF16 else "f32"
+    check(out[keep], ref[keep], None, path, "other tokens")
+
+
+@pytest.mark.parametrize("T", [128, 129])
+def test_layer_inline_limit(T):
+    """T x 8 = 1024 pairs: two launches, the pass grouping derived inside the
+    gate+up blocks; 1032 pairs: the preparation kernel's plan records.  16
+    experts, so most experts have many pairs (four tokens per pass)."""
+    say(f"layer f32 E=16 H=256 F=128 T={T} k=8")
+    L = Layer(16, 256, 128, seed=507)
+    g = synth.generator(508 + T)
+    x = synth.rand_x(g, (T, 256))
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, T, 16), 8)
+    ids[3, 0] = -1
+    ids[7, 2] = ids[7, 1]
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
+
+
+@pytest.mark.parametrize("counts_e", [16, 48, 1024])
+def test_layer_pass_grouping(counts_e):
+    """Experts with 1..17 pairs (duplicates in one token included) at expert
+    counts that select four, two and one tokens per weight pass."""
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 16, 17]
+    T = sum(counts)
+    E = counts_e
+    say(f"layer f32 E={E} H=192 F=320 T={T} k=2, fixed pairs per expert")
+    L = Layer(E, 192, 320, seed=509)
+    perm = torch.randperm(2 * T, generator=torch.Generator().manual_seed(509))
+    assign = torch.repeat_interleave(torch.arange(len(counts)), torch.tensor(counts) * 2)[perm]
+    ids = (assign * (E // 16)).to(torch.int32).view(T, 2)
+    g = synth.generator(510)
+    x = synth.rand_x(g, (T, 192))
+    w = torch.rand((T, 2), generator=g)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
+
+
+@pytest.mark.parametrize("E,H,F,T", [(16, 256, 128, 37), (128, 4096, 1536, 16)])
+def test_digit_variant_layer(E, H, F, T):
+    say(f"digit variant layer E={E} H={H} F={F} T={T}")
+    L = Layer(E, H, F, seed=511, gen_device=DEV if E > 16 else "cpu")
+    g = synth.generator(512)
+    x = synth.rand_x(g, (T, H))
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, T, E), 8 if E > 16 else 4)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV),
+                        x_dtype=qm.QMOE_F32_DIGITS).cpu().numpy()
+    ref = L.oracle_layer(x, ids, w)
+    err = rel_l2(out, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= F32_TOL
+
+
+def test_digit_variant_expert_ffn():
+    say("digit variant expert ffn H=4096 F=1536 batch 3")
+    L = Layer(1, 4096, 1536, seed=513)
+    x = synth.rand_x(synth.generator(514), (3, 4096))
+    out = qm.qmoe_expert_ffn(L.packed["qg"][0], L.s_dev["sg"][0], L.packed["qu"][0],
+                             L.s_dev["su"][0], L.packed["qd"][0], L.s_dev["sd"][0], 4096, 1536,
+                             x.to(DEV), x_dtype=qm.QMOE_F32_DIGITS).cpu().numpy()
+    ref = L.oracle_layer(x, torch.zeros(3, 1, dtype=torch.int32), torch.ones(3, 1))
+    assert rel_l2(out, ref) <= F32_TOL

@@ -50,6 +50,14 @@ MUTANTS = [
     ("import_xor_low_nibble_only", "packed[b] = (uint8_t)(twos[b] ^ 0x88);",
      "packed[b] = (uint8_t)(twos[b] ^ 0x08);"),
     ("detect_group_largest_first", "for (int c = 0; c < 8; c++)", "for (int c = 7; c >= 0; c--)"),
+    ("dsilu_missing_factor", "return sg * (1.0 + z * (1.0 - sg));", "return sg * (1.0 + z * sg);"),
+    ("matvec_abs_signed", "acc += fabs(orc_weight(packed, scales, cols, gs, o, i) *",
+     "acc += (orc_weight(packed, scales, cols, gs, o, i) *"),
+    ("layer_mag_h_once", "c[f] = 2.0 * fabs(h) +", "c[f] = fabs(h) +"),
+    ("layer_mag_no_gate_term", "fabs(orc_dsilu(g[f]) * u[f]) * ag[f] +", "0.0 * ag[f] +"),
+    ("layer_mag_up_uses_gate", "fabs(orc_silu(g[f])) * au[f];", "fabs(orc_silu(g[f])) * ag[f];"),
+    ("layer_mag_signed_weight", "double wt = fabs((double)w[t * k + s]);",
+     "double wt = (double)w[t * k + s];"),
 ]
 
 
