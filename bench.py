@@ -6,20 +6,23 @@ are resident in HBM before timing starts:
 
   * one grouped-int4 matvec (W 256 x 1024, f32 x);
   * decode layers (128 experts, hidden 4096, intermediate 1536, top-8,
-    f32 activations) at 1, 4 and 16 tokens, CALLS calls each.  Every call
-    uses a fresh routing draw and the next of REPLICAS copies of the weights
-    (REPLICAS x 1.36 GB >> the 256 MB Infinity Cache), so no call is served
-    from a cache warmed by the previous one.  These calls are captured once in
-    a HIP graph and replayed, because a 10-100 us layer is shorter than the
-    host-side cost of issuing it;
+    f32 activations, f32 arithmetic) at 1, 4 and 16 tokens, CALLS calls each.
+    Every call uses a fresh routing draw and the next of REPLICAS copies of
+    the weights (REPLICAS x 1.36 GB >> the 256 MB Infinity Cache), so no call
+    is served from a cache warmed by the previous one.  These calls are
+    captured once in a HIP graph and replayed, because a 10-200 us layer is
+    shorter than the host-side cost of issuing it;
   * one 8192-token prefill layer (same layer shape, bf16 activations,
     uniform-random router logits) on the MFMA path.
 
 Reported: % of roofline over the step (sum of per-call roofline times over
 measured time), decode GB/s, prefill TFLOP/s, the roofline record of the
-dominant kernel (prefill gate+up, timed with HIP events recorded between the
-layer's phases on the stream it runs on), and the CPU oracle timed on a
-bounded sample of the same workload.
+dominant kernel (timed with HIP events recorded between the layer's phases
+on the stream it runs on), and the CPU oracle timed on a bounded sample of
+the same workload (one core and all cores).  Outside the step: the single
+expert, the 256-expert Zipf layer (64-token decode, 2048-token prefill), the
+digit variant of the decode path, the router, host-resident experts and
+other group sizes, each as its own labelled record.
 """
 from __future__ import annotations
 
@@ -49,21 +52,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_alg(ids, T):
-    uniq = len(set(int(e) for e in ids.flatten().tolist() if 0 <= int(e) < E))
-    pairs = sum(1 for e in ids.flatten().tolist() if 0 <= int(e) < E)
-    nbytes = uniq * EXPERT_BYTES + T * H * 4 * 2 + T * K * 8
-    flops = 2.0 * pairs * 3 * H * F
+def layer_bytes_per_expert(hidden, inter, group=64):
+    """Packed codes + f32 scales of one expert's gate, up and down."""
+    gu = inter * hidden // 2 + inter * (-(-hidden // group)) * 4
+    dn = hidden * inter // 2 + hidden * (-(-inter // group)) * 4
+    return 2 * gu + dn
+
+
+def decode_alg(ids, T, experts=E, hidden=H, inter=F, k=K):
+    """Algorithmic bytes (each touched expert's weights once, x in, out,
+    routing) and flops of one f32 decode call, and its roofline time."""
+    flat = [int(e) for e in ids.flatten().tolist()]
+    uniq = len(set(e for e in flat if 0 <= e < experts))
+    pairs = sum(1 for e in flat if 0 <= e < experts)
+    nbytes = uniq * layer_bytes_per_expert(hidden, inter) + T * hidden * 4 * 2 + T * k * 8
+    flops = 2.0 * pairs * 3 * hidden * inter
     return nbytes, flops, max(nbytes / HBM_PEAK, flops / F32_PEAK)
 
 
-def prefill_alg(ids, T):
+def decode_gateup_bytes(ids, T, experts=E, hidden=H, inter=F):
+    """Algorithmic bytes of the decode gate+up launch: gate and up weights
+    of each touched expert once, plus x."""
+    uniq = len(set(int(e) for e in ids.flatten().tolist() if 0 <= int(e) < experts))
+    gu = inter * hidden // 2 + inter * (-(-hidden // 64)) * 4
+    return uniq * 2 * gu + T * hidden * 4
+
+
+def prefill_alg(ids, T, experts=E, hidden=H, inter=F, k=K):
     flat = ids.flatten()
-    valid = flat[(flat >= 0) & (flat < E)]
+    valid = flat[(flat >= 0) & (flat < experts)]
     uniq = int(valid.unique().numel())
-    nbytes = uniq * EXPERT_BYTES + T * H * 2 + T * H * 4 + T * K * 8
-    flops = 2.0 * int(valid.numel()) * 3 * H * F
-    gateup_flops = 2.0 * int(valid.numel()) * 2 * H * F
+    nbytes = (uniq * layer_bytes_per_expert(hidden, inter) + T * hidden * 2 + T * hidden * 4 +
+              T * k * 8)
+    flops = 2.0 * int(valid.numel()) * 3 * hidden * inter
+    gateup_flops = 2.0 * int(valid.numel()) * 2 * hidden * inter
     return nbytes, flops, gateup_flops, max(nbytes / HBM_PEAK, flops / BF16_PEAK)
 
 
@@ -87,10 +109,10 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_srcs):
-    """HBM traffic per launch from the committed counter summary, if it was
-    taken on the current kernel sources (null otherwise)."""
-    path = os.path.join(ROOT, "profiles", "mfma_gateup_prefill_e128_t8192_counters.md")
+def load_traffic(kernel_srcs, name="mfma_gateup_prefill_e128_t8192_counters.md"):
+    """HBM traffic per launch from the committed counter summary `name`, if
+    it was taken on the current kernel sources (null otherwise)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     h = source_hash(kernel_srcs)
@@ -103,12 +125,34 @@ def load_traffic(kernel_srcs):
     return None
 
 
+def host_cpu():
+    """(model name, usable cores) of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    return model or platform.processor() or platform.machine(), cores
+
+
 def cpu_baseline(qm, synth, oracle, layers_codes, layers_scales, decode_inputs, prefill_in,
                  mv, roof_step):
-    """The oracle, untouched, on a bounded sample of the same workload."""
+    """The oracle, untouched, on a bounded sample of the same workload: one
+    core (the oracle's own layer) and all cores (the same layer over tokens
+    under OpenMP).  Decode calls are timed in full; prefill on a seeded
+    sample of tokens, extrapolated per token to all 8192."""
     import numpy as np
     import torch
     orc = oracle.Oracle()
+    host_model, host_cores = host_cpu()
 
     def subset(codes, scales, used):
         sel = torch.as_tensor(used, dtype=torch.long)
@@ -119,41 +163,68 @@ def cpu_baseline(qm, synth, oracle, layers_codes, layers_scales, decode_inputs, 
             out.append(scales[ks].index_select(0, sel.to(scales[ks].device)).cpu().numpy())
         return out
 
-    def run_layer(codes, scales, x, ids, w):
+    def run_layer(codes, scales, x, ids, w, omp):
         used = sorted(set(int(e) for e in ids.flatten().tolist() if 0 <= int(e) < E))
         remap = {e: i for i, e in enumerate(used)}
         ids2 = np.vectorize(lambda e: remap.get(int(e), -1))(ids.numpy()).astype(np.int32)
         st = subset(codes, scales, used)
         t0 = time.perf_counter()
-        orc.layer(st[0], st[1], st[2], st[3], st[4], st[5], H, F, x, ids2, w.numpy())
-        return time.perf_counter() - t0
+        if omp:
+            _, _, threads = oracle.layer_omp(*st, H, F, x, ids2, w.numpy())
+        else:
+            orc.layer(*st, H, F, x, ids2, w.numpy())
+            threads = 1
+        return time.perf_counter() - t0, threads
 
-    # matvec: full
+    # matvec: in full (a few ms; not worth threading)
     q, s, x = mv
     pq = orc.pack(q.cpu().numpy())[0]
     t0 = time.perf_counter()
     orc.matvec(pq, s.cpu().numpy(), MATVEC[1], x.cpu().numpy())
     t_mv = time.perf_counter() - t0
-    # decode: the first call at T=1 and T=4 in full; T=16 from the T=4 per-token time
-    x1, i1, w1 = decode_inputs[1][0]
-    t_d1 = run_layer(layers_codes[0], layers_scales[0], x1, i1, w1)
-    x4, i4, w4 = decode_inputs[4][0]
-    t_d4 = run_layer(layers_codes[0], layers_scales[0], x4, i4, w4)
-    # prefill: 4 sampled tokens
     xp, ip, wp = prefill_in
-    toks = [0, 2047, 4096, 8191]
-    t_p = run_layer(layers_codes[-1], layers_scales[-1], xp[toks], ip[toks], wp[toks])
-    per_tok_p = t_p / len(toks)
-    cpu_step = (t_mv + CALLS * (t_d1 + t_d4 + 4 * t_d4) + per_tok_p * PREFILL_T)
-    sample_s = t_mv + t_d1 + t_d4 + t_p
+    legs = {}
+    for omp in (False, True):
+        threads = 1
+        t_dec = {}
+        for T in ((1, 4) if not omp else DECODE_T):
+            xt, it, wt = decode_inputs[T][0]
+            t_dec[T], th = run_layer(layers_codes[0], layers_scales[0], xt, it, wt, omp)
+            threads = max(threads, th)
+        if not omp:
+            t_dec[16] = 4 * t_dec[4]          # per-token extrapolation from 4 tokens
+        # prefill: a seeded sample of tokens, 4 per thread
+        n_sample = 4 * (threads if omp else 1)
+        toks = torch.randperm(PREFILL_T, generator=torch.Generator().manual_seed(5))[:n_sample]
+        toks = sorted(int(t) for t in toks)
+        t_p, th = run_layer(layers_codes[-1], layers_scales[-1], xp[toks], ip[toks], wp[toks],
+                            omp)
+        threads = max(threads, th)
+        cpu_step = t_mv + CALLS * sum(t_dec[T] for T in DECODE_T) + t_p / len(toks) * PREFILL_T
+        legs[omp] = dict(
+            value=round(100.0 * roof_step / cpu_step, 6), unit="% of roofline",
+            cores=threads, cpu_step_s=round(cpu_step, 2),
+            decode_call_s={f"t{T}": round(v, 3) for T, v in t_dec.items()},
+            prefill_s_per_token=round(t_p / len(toks), 4), prefill_sample_tokens=len(toks),
+            sample_wall_s=round(t_mv + sum(v for T, v in t_dec.items()
+                                           if omp or T != 16) + t_p, 1))
+    one, allc = legs[False], legs[True]
     return dict(
-        value=100.0 * roof_step / cpu_step, unit="% of roofline", cores=1, kind="oracle",
-        sample=(f"oracle (scalar C, fp64, 1 thread) on: the matvec in full, the first decode "
-                f"call at 1 and 4 tokens in full, 4 of the 8192 prefill tokens; decode at 16 "
-                f"tokens and the rest of prefill extrapolated per token "
-                f"({sample_s:.1f} s of CPU work)"),
-        cpu_step_s=cpu_step, host=platform.processor() or platform.machine(),
-        host_cpus=os.cpu_count())
+        value=allc["value"], unit="% of roofline", cores=allc["cores"], kind="oracle",
+        sample=(f"oracle (scalar C, fp64) on all {allc['cores']} threads (OpenMP over tokens): "
+                f"the matvec and the first decode call at 1, 4 and 16 tokens in full, "
+                f"{allc['prefill_sample_tokens']} seeded prefill tokens of 8192 extrapolated "
+                f"per token; {CALLS} decode calls per batch size extrapolated from the first "
+                f"({allc['sample_wall_s']} s wall)"),
+        cpu_step_s=allc["cpu_step_s"], decode_call_s=allc["decode_call_s"],
+        prefill_s_per_token=allc["prefill_s_per_token"],
+        single_core=dict(
+            value=one["value"], cores=1, cpu_step_s=one["cpu_step_s"],
+            decode_call_s=one["decode_call_s"], prefill_s_per_token=one["prefill_s_per_token"],
+            sample=(f"one thread: the matvec, the first decode call at 1 and 4 tokens in full "
+                    f"(16 tokens extrapolated per token from 4), {one['prefill_sample_tokens']} "
+                    f"seeded prefill tokens ({one['sample_wall_s']} s)")),
+        host=host_model, host_cores=host_cores)
 
 
 def time_router(qm, synth, torch, dev, reps=20):
@@ -191,33 +262,207 @@ def time_router(qm, synth, torch, dev, reps=20):
     return res
 
 
-def time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t, reps=3):
+def new_events(torch, n):
+    """n timing events whose HIP events exist (torch creates them lazily, on
+    the first record) so their handles can be passed to qmoe_layer_ex."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for ev in evs:
+        ev.record()
+    return evs
+
+
+def time_graph(torch, fn, reps=3):
+    """Capture fn() in a HIP graph, replay it once untimed, then return the
+    best of `reps` timed replays in ms (events on the current stream)."""
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        fn()
+    graph.replay()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del graph
+    return best
+
+
+def time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t, reps=3, x_dtype=None):
     """The step's decode calls split by batch size: each batch size's calls
-    captured in a graph of their own and replayed.  Not part of the step."""
+    captured in a graph of their own and replayed.  Not part of the step.
+    x_dtype selects the path (None: f32 arithmetic)."""
     res = {}
     for T, calls in decode_dev.items():
         def run():
             for c in calls:
-                qm.qmoe_layer(c["layer"], c["x"], c["ids"], c["w"], out=c["out"], ws=c["ws"])
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
-            run()
-        graph.replay()
-        best = None
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            graph.replay()
-            b.record()
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b)
-            best = ms if best is None else min(best, ms)
-        del graph
+                qm.qmoe_layer(c["layer"], c["x"], c["ids"], c["w"], out=c["out"],
+                              ws=c["ws_dig" if x_dtype is not None else "ws"], x_dtype=x_dtype)
+        best = time_graph(torch, run, reps)
         res[f"t{T}"] = {"us_per_call": round(best * 1e3 / len(calls), 1),
                         "GBps": round(bytes_by_t[T] / (best * 1e-3) / 1e9, 1),
                         "frac_of_hbm_roofline": round(bytes_by_t[T] / HBM_PEAK / (best * 1e-3), 4)}
+    return res
+
+
+def time_decode_phases(qm, torch, decode_dev, gu_bytes_by_t):
+    """Per-launch times of the f32 decode kernels: every call of each batch
+    size issued eagerly through qmoe_layer_ex with HIP events between its
+    phases (recorded on the stream the kernels run on); returns per batch
+    size the mean gate+up and down launch times and the gate+up launch's
+    achieved algorithmic GB/s."""
+    res = {}
+    for T, calls in decode_dev.items():
+        evs = [new_events(torch, 4) for _ in calls]
+        for c, ev in zip(calls, evs):       # warm up, materialise the events
+            qm.qmoe_layer_ex(c["layer"], c["x"], c["ids"], c["w"], ev, out=c["out"], ws=c["ws"])
+        torch.cuda.synchronize()
+        for c, ev in zip(calls, evs):
+            qm.qmoe_layer_ex(c["layer"], c["x"], c["ids"], c["w"], ev, out=c["out"], ws=c["ws"])
+        torch.cuda.synchronize()
+        gu = sum(ev[1].elapsed_time(ev[2]) for ev in evs) / len(evs)
+        dn = sum(ev[2].elapsed_time(ev[3]) for ev in evs) / len(evs)
+        res[f"t{T}"] = {"gateup_us": round(gu * 1e3, 2), "down_us": round(dn * 1e3, 2),
+                        "gateup_GBps": round(gu_bytes_by_t[T] / len(calls) / (gu * 1e-3) / 1e9,
+                                             1)}
+    return res
+
+
+def time_expert_ffn(qm, synth, torch, dev, copies=64, reps=3):
+    """The single expert (hidden 4096, intermediate 1536, f32 x [1 x 4096]):
+    one qmoe_expert_ffn call per copy of the expert's weights, `copies`
+    copies (680 MB) so that no call is served by a cache warmed by the
+    previous one, captured in a graph.  Not part of the step."""
+    g = synth.generator(synth.EXPERT["seed"], dev)
+    w = synth.layer_weights(g, copies, H, F, device=dev)
+    pk = {k: qm.qmoe_pack(w[k]) for k in ("qg", "qu", "qd")}
+    x = synth.rand_x(synth.generator(synth.EXPERT["seed"]), (1, H)).to(dev)
+    out = torch.empty(1, H, device=dev)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+
+    def run():
+        for i in range(copies):
+            qm.qmoe_expert_ffn(pk["qg"][i], w["sg"][i], pk["qu"][i], w["su"][i], pk["qd"][i],
+                               w["sd"][i], H, F, x, out=out, ws=ws)
+    best = time_graph(torch, run, reps)
+    us = best * 1e3 / copies
+    nbytes = EXPERT_BYTES + H * 4 * 2
+    roof = nbytes / HBM_PEAK
+    res = {"workload": "expert_ffn_h4096_f1536 (batch 1, f32)", "us_per_call": round(us, 2),
+           "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "frac_of_hbm_roofline": round(roof / (us * 1e-6), 4), "alg_bytes": nbytes,
+           "calls": copies}
+    del pk, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_layer_e256(qm, synth, torch, dev, calls=16, reps=3):
+    """The large skewed layer: 256 experts, hidden 6144, intermediate 2048,
+    Zipf(1.1) routing, decode at 64 tokens (f32; `calls` calls with fresh
+    routing, captured in a graph) and prefill at 2048 tokens (bf16; one call
+    timed with events).  Not part of the step."""
+    E2, H2, F2 = 256, 6144, 2048
+    g = synth.generator(4, dev)
+    w = synth.layer_weights(g, E2, H2, F2, device=dev)
+    pk = {k: qm.qmoe_pack(w[k]) for k in ("qg", "qu", "qd")}
+    del g
+    layer = qm.QLayer(pk["qg"], w["sg"], pk["qu"], w["su"], pk["qd"], w["sd"], H2, F2)
+    del w["qg"], w["qu"], w["qd"]
+    res = {}
+    # decode, 64 tokens
+    wl = synth.LAYERS["decode_e256_t64_zipf"]
+    gen = synth.generator(wl.seed)
+    dec, nbytes, flops, roof, gu_bytes = [], 0, 0.0, 0.0, 0
+    for _ in range(calls):
+        x, ids, wt = synth.layer_inputs(wl, gen)
+        nb, fl, rt = decode_alg(ids, 64, E2, H2, F2)
+        nbytes, flops, roof = nbytes + nb, flops + fl, roof + rt
+        gu_bytes += decode_gateup_bytes(ids, 64, E2, H2, F2)
+        dec.append(dict(x=x.to(dev), ids=ids.to(dev), w=wt.to(dev),
+                        out=torch.empty(64, H2, device=dev)))
+    wsd = torch.empty(layer.workspace_bytes(64, K, qm.QMOE_F32), dtype=torch.uint8, device=dev)
+
+    def run_dec():
+        for c in dec:
+            qm.qmoe_layer(layer, c["x"], c["ids"], c["w"], out=c["out"], ws=wsd)
+    best = time_graph(torch, run_dec, reps)
+    us = best * 1e3 / calls
+    evs = [new_events(torch, 4) for _ in dec]
+    for _ in range(2):
+        for c, ev in zip(dec, evs):
+            qm.qmoe_layer_ex(layer, c["x"], c["ids"], c["w"], ev, out=c["out"], ws=wsd)
+        torch.cuda.synchronize()
+    gu = sum(ev[1].elapsed_time(ev[2]) for ev in evs) / calls
+    dn = sum(ev[2].elapsed_time(ev[3]) for ev in evs) / calls
+    res["decode_t64_f32"] = {
+        "us_per_call": round(us, 1), "GBps": round(nbytes / (best * 1e-3) / 1e9, 1),
+        "frac_of_roofline": round(roof / (best * 1e-3), 4), "alg_bytes_per_call": nbytes // calls,
+        "gateup_us": round(gu * 1e3, 1), "down_us": round(dn * 1e3, 1),
+        "gateup_GBps": round(gu_bytes / calls / (gu * 1e-3) / 1e9, 1), "calls": calls}
+    # prefill, 2048 tokens
+    wlp = synth.LAYERS["prefill_e256_t2048_zipf"]
+    xp, ip, wp = synth.layer_inputs(wlp, synth.generator(wlp.seed))
+    pb, pf, pgu, proof = prefill_alg(ip, 2048, E2, H2, F2)
+    xp, ip, wp = xp.to(dev), ip.to(dev), wp.to(dev)
+    op = torch.empty(2048, H2, device=dev)
+    wsp = torch.empty(layer.workspace_bytes(2048, K, qm.QMOE_BF16), dtype=torch.uint8,
+                      device=dev)
+    evs = new_events(torch, 5)
+    qm.qmoe_layer_ex(layer, xp, ip, wp, evs, out=op, ws=wsp)
+    best, ph = None, None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        qm.qmoe_layer_ex(layer, xp, ip, wp, evs, out=op, ws=wsp)
+        torch.cuda.synchronize()
+        ms = evs[0].elapsed_time(evs[4])
+        if best is None or ms < best:
+            best, ph = ms, [evs[j].elapsed_time(evs[j + 1]) for j in range(4)]
+    res["prefill_t2048_bf16"] = {
+        "ms": round(best, 4), "GBps": round(pb / (best * 1e-3) / 1e9, 1),
+        "TFLOPs": round(pf / (best * 1e-3) / 1e12, 1),
+        "frac_of_roofline": round(proof / (best * 1e-3), 4),
+        "bound": "hbm" if pb / HBM_PEAK > pf / BF16_PEAK else "mfma",
+        "alg_bytes": pb, "alg_flops": pf,
+        "phase_ms": {"worklist": round(ph[0], 4), "gate_up": round(ph[1], 4),
+                     "down": round(ph[2], 4), "combine": round(ph[3], 4)}}
+    res["config"] = {"workload": "layer_e256_h6144_f2048_top8_zipf1.1", "experts": E2,
+                     "hidden": H2, "inter": F2, "topk": K}
+    del layer, pk, w, wsd, wsp
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_probe(torch, dev, reps=5):
+    """Plain device streams at the decode working-set sizes: a read (sum of
+    an f32 buffer) and a copy, each over a set of buffers whose total exceeds
+    the Infinity Cache, so every pass reads from HBM.  GB/s per size (the
+    read counts the bytes read, the copy bytes read + written)."""
+    res = {}
+    for mb in (56, 85, 290, 1024):
+        n = mb * (1 << 20) // 4
+        nbuf = max(2, -(-2048 // mb))
+        bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(nbuf)]
+        dst = torch.empty(n, dtype=torch.float32, device=dev)
+        acc = torch.empty(nbuf, dtype=torch.float32, device=dev)
+        for name in ("read", "copy"):
+            def run():
+                for i, b in enumerate(bufs):
+                    if name == "read":
+                        torch.sum(b, dim=0, out=acc[i])
+                    else:
+                        dst.copy_(b)
+            best = time_graph(torch, run, reps)
+            moved = nbuf * n * 4 * (1 if name == "read" else 2)
+            res[f"{name}_{mb}MB"] = round(moved / (best * 1e-3) / 1e9, 1)
+        del bufs, dst, acc
+        torch.cuda.empty_cache()
     return res
 
 
@@ -404,6 +649,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times and exit "
                          "(reference for HBM byte counters)")
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="time plain device reads and copies at 56 MB, 85 MB, 290 MB and "
+                         "1 GB (the HBM rates the decode fractions sit beside) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -425,6 +673,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": a.numel() * 4}))
+        return
+    if args.stream_probe:
+        print(json.dumps({"stream_probe_GBps": stream_probe(torch, dev)}), flush=True)
         return
 
     # ---------------- inputs, resident in HBM before timing ----------------
@@ -452,16 +703,17 @@ def main():
     roof_step += (MATVEC[0] * MATVEC[1] // 2 + MATVEC[0] * MATVEC[1] // 64 * 4 +
                   MATVEC[1] * 4 + MATVEC[0] * 4) / HBM_PEAK
     dec_bytes += MATVEC[0] * MATVEC[1] // 2 + MATVEC[0] * MATVEC[1] // 64 * 4 + MATVEC[1] * 8
-    bytes_by_t = {}
+    bytes_by_t, gu_bytes_by_t = {}, {}
     for T in DECODE_T:
         wl = synth.LAYERS[f"decode_e128_t{T}"]
         gen = synth.generator(wl.seed)
         decode_inputs[T], decode_dev[T] = [], []
-        bytes_by_t[T] = 0
+        bytes_by_t[T] = gu_bytes_by_t[T] = 0
         for i in range(CALLS):
             x, ids, w = synth.layer_inputs(wl, gen)
             nb, fl, rt = decode_alg(ids, T)
             bytes_by_t[T] += nb
+            gu_bytes_by_t[T] += decode_gateup_bytes(ids, T)
             dec_bytes += nb
             dec_flops += fl
             roof_step += rt
@@ -471,7 +723,9 @@ def main():
                 layer=lay, x=x.to(dev), ids=ids.to(dev), w=w.to(dev),
                 out=torch.empty(T, H, device=dev),
                 ws=torch.empty(lay.workspace_bytes(T, K, qm.QMOE_F32), dtype=torch.uint8,
-                               device=dev)))
+                               device=dev),
+                ws_dig=torch.empty(lay.workspace_bytes(T, K, qm.QMOE_F32_DIGITS),
+                                   dtype=torch.uint8, device=dev)))
     wlp = synth.LAYERS["prefill_e128_t8192"]
     genp = synth.generator(wlp.seed)
     xp, ip, wp = synth.layer_inputs(wlp, genp)
@@ -552,8 +806,43 @@ def main():
     value = 100.0 * roof_step / (ms_step * 1e-3)
     dec_roof = roof_step - p_roof
     achieved = p_gu_flops / (gateup_ms * 1e-3)
-    kernel_src = [os.path.join(ROOT, "grouped_int4_expert_amd", "csrc", f)
-                  for f in ("mfma_gateup.h", "mfma_loop.h", "mfma.hip")]
+    csrc = os.path.join(ROOT, "grouped_int4_expert_amd", "csrc")
+    kernel_src = [os.path.join(csrc, f) for f in ("mfma_gateup.h", "mfma_loop.h", "mfma.hip")]
+    # per-launch times of the decode kernels (eager calls with phase events)
+    phases = time_decode_phases(qm, torch, decode_dev, gu_bytes_by_t)
+    dec_gu_ms = CALLS * sum(phases[f"t{T}"]["gateup_us"] for T in DECODE_T) * 1e-3
+    dec_gu_bytes = sum(gu_bytes_by_t.values())
+    dec_gu_launches = CALLS * len(DECODE_T)
+    roof_prefill = {
+        "kernel": "mfma_gateup_kernel (prefill gate+up, 8192 tokens)",
+        "bound": "mfma",
+        "achieved": round(achieved / 1e12, 1),
+        "peak": round(BF16_PEAK / 1e12, 1),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / BF16_PEAK, 4),
+        "traffic": load_traffic(kernel_src),
+        "alg_flops_per_launch": p_gu_flops,
+        "avg_launch_ms": round(gateup_ms, 4),
+        "ms_per_step": round(gateup_ms, 4),
+    }
+    dec_achieved = dec_gu_bytes / (dec_gu_ms * 1e-3)
+    roof_decode = {
+        "kernel": (f"f32_gateup_kernel (decode gate+up, 128 experts, {CALLS} launches at each "
+                   f"of 1, 4 and 16 tokens)"),
+        "bound": "hbm",
+        "achieved": round(dec_achieved / 1e9, 1),
+        "peak": round(HBM_PEAK / 1e9, 1),
+        "unit": "GB/s",
+        "frac": round(dec_achieved / HBM_PEAK, 4),
+        "traffic": load_traffic([os.path.join(csrc, "gemv_f32.hip")],
+                                "f32_gateup_decode_e128_counters.md"),
+        "alg_bytes_per_launch": dec_gu_bytes // dec_gu_launches,
+        "avg_launch_ms": round(dec_gu_ms / dec_gu_launches, 5),
+        "ms_per_step": round(dec_gu_ms, 4),
+    }
+    # the dominant kernel: the one that takes the most time in a step
+    dominant, other = ((roof_decode, roof_prefill) if dec_gu_ms > gateup_ms
+                       else (roof_prefill, roof_decode))
     rec = {
         "metric": "int4-g64 MoE expert GB/s (decode) + TFLOP/s (8K prefill), % of roofline",
         "value": round(value, 3),
@@ -565,7 +854,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16/f16 MFMA (prefill); i4 x i4 -> i32 dot, f32 scale+accumulate (decode)",
+        "dtype": ("f32 (decode: int4 codes unpacked to f32, f32 FMA, f32 group scale); "
+                  "bf16 x as f16 MFMA operands, f32 accumulate (prefill)"),
         "data": "synthetic",
         "config": {
             "workload": ("matvec_256x1024 + decode_e128_h4096_f1536_top8 (T=1,4,16; "
@@ -580,6 +870,8 @@ def main():
             "frac_of_hbm_roofline": round(dec_roof / (dec_ms * 1e-3), 4),
             "ms": round(dec_ms, 4),
             "alg_bytes": int(dec_bytes),
+            "arithmetic": "f32",
+            "kernel_us": phases,
         },
         "prefill": {
             "TFLOPs": round(p_flops / (pre_ms * 1e-3) / 1e12, 1),
@@ -589,20 +881,21 @@ def main():
                          "down": round(ph[2], 4), "combine": round(ph[3], 4)},
             "alg_flops": p_flops,
         },
-        "roofline": {
-            "kernel": "mfma_gateup_kernel (prefill gate+up, 8192 tokens)",
-            "bound": "mfma",
-            "achieved": round(achieved / 1e12, 1),
-            "peak": round(BF16_PEAK / 1e12, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / BF16_PEAK, 4),
-            "traffic": load_traffic(kernel_src),
-            "alg_flops_per_launch": p_gu_flops,
-            "avg_launch_ms": round(gateup_ms, 4),
-        },
+        "roofline": dominant,
+        "roofline_next_kernel": other,
     }
     if not args.no_extras:
+        log("decode by batch size ...")
         rec["decode"]["by_tokens"] = time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t)
+        rec["decode_digits_variant"] = {
+            "note": ("QMOE_F32_DIGITS: activations rounded to 18-bit block fixed point, "
+                     "int4 x int4 dot products; not the f32 arithmetic of the headline"),
+            "by_tokens": time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t,
+                                               x_dtype=qm.QMOE_F32_DIGITS)}
+        log("single expert ...")
+        rec["expert_ffn"] = time_expert_ffn(qm, synth, torch, dev)
+        log("256-expert Zipf layer ...")
+        rec["layer_e256_zipf"] = time_layer_e256(qm, synth, torch, dev)
         rec["router"] = time_router(qm, synth, torch, dev)
         rec["host_experts"] = time_host_experts(qm, synth, torch, dev, replicas[0])
         rec["group_sizes"] = time_formats(qm, synth, torch, dev)

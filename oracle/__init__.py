@@ -42,6 +42,56 @@ def build(cflags=None, out=None) -> str:
     return out
 
 
+_OMP_SRC = os.path.join(_HERE, "baseline_omp.c")
+_OMP_LIB = os.path.join(_HERE, "liboracle_omp.so")
+_omp = None
+
+
+def build_omp(out=None) -> str:
+    """The same oracle source plus the all-cores baseline driver (an OpenMP
+    parallel for over tokens around the unchanged orc_layer), in a library
+    of its own: used only by the benchmark's CPU-baseline leg."""
+    out = out or _OMP_LIB
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+           "-std=c99", "-Wall", "-Werror", "-fopenmp", _SRC, _OMP_SRC, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load_omp():
+    global _omp
+    if _omp is not None:
+        return _omp
+    if not os.path.exists(_OMP_LIB):
+        build_omp()
+    lib = ctypes.CDLL(_OMP_LIB)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.orc_layer_omp.restype = i64
+    lib.orc_layer_omp.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, i64, vp, vp,
+                                  i64, vp]
+    lib.orc_omp_threads.restype = ctypes.c_int
+    lib.orc_omp_threads.argtypes = []
+    _omp = lib
+    return lib
+
+
+def layer_omp(pg, sg, pu, su, pd, sd, hidden, inter, x, ids, w, gs=64):
+    """orc_layer over all tokens on all host cores (OpenMP over tokens).
+    Returns (out, n_invalid, threads)."""
+    lib = load_omp()
+    pg, pu, pd = (_c(_np(a), np.uint8) for a in (pg, pu, pd))
+    sg, su, sd = (_c(_np(a), np.float32) for a in (sg, su, sd))
+    experts = pg.shape[0]
+    x = _c(_np(x), np.float64).reshape(-1, hidden)
+    ids = _c(_np(ids), np.int32)
+    w = _c(_np(w), np.float32)
+    tokens, k = ids.shape
+    out = np.empty((tokens, hidden), dtype=np.float64)
+    bad = lib.orc_layer_omp(_p(pg), _p(sg), _p(pu), _p(su), _p(pd), _p(sd), experts, hidden,
+                            inter, gs, _p(x), tokens, _p(ids), _p(w), k, _p(out))
+    return out, int(bad), int(lib.orc_omp_threads())
+
+
 def load(path=None):
     """Load (building once if missing) and declare the C signatures."""
     global _lib

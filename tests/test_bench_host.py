@@ -57,3 +57,15 @@ def test_traffic_needs_the_current_sources(tmp_path):
     a = bench.source_hash([str(src)])
     src.write_text("// changed\n")
     assert bench.source_hash([str(src)]) != a
+
+
+def test_expert_bytes_of_the_large_layer():
+    # hidden 6144 / inter 2048: the pages' "19 megs" packed, "22 megs" with scales
+    assert bench.layer_bytes_per_expert(6144, 2048) == 21_233_664
+    assert bench.layer_bytes_per_expert(4096, 1536) == bench.EXPERT_BYTES
+
+
+def test_decode_gateup_bytes_count_gate_and_up_once_per_expert():
+    ids = torch.tensor([[0, 1, 1, 200], [1, -1, 0, 3]])
+    gu = 1536 * 4096 // 2 + 1536 * 64 * 4
+    assert bench.decode_gateup_bytes(ids, 2) == 3 * 2 * gu + 2 * 4096 * 4
