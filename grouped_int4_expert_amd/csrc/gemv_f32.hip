@@ -1,8 +1,7 @@
 // Decode GEMVs in f32 arithmetic (f32 activations): grouped int4 weights are
 // streamed once per expert with 128-bit buffer loads, every code is unpacked
 // in registers to an exact f32, multiplied with the f32 activation in an f32
-// FMA chain, scaled once per group by its f32 scale and reduced across lanes
-// with DPP.
+// FMA chain, scaled by its f32 group scale and reduced across lanes with DPP.
 //
 // What is computed follows the colibri pull request "cuda+engine: full fmt=4
 // (grouped int4 gs=64) support": the per-group scale scales[o*ng + i/gs]
@@ -23,12 +22,14 @@
 // one per row), so each lane needs one scale per row, at index
 // (32 * chunk) >> log2(group).
 //
-// Unpack: with w' = w ^ 0x88888888 (offset nibbles -> two's complement),
-// (w' & 0xF0F0F0F0) holds 16*q of the odd elements as signed bytes and
-// ((w' << 4) & 0xF0F0F0F0) 16*q of the even ones; each byte converts to f32
-// in one sign-extending instruction, and the factor 16 (a power of two) is
-// taken out of the row sum at the end.  11 VALU instructions per 8 codes,
-// then one FMA per code and token.
+// Unpack: w' = w ^ 0x88888888 turns the offset nibbles into two's
+// complement; (w' & 0xF0F0F0F0) then holds 16 q of the odd elements as signed
+// bytes and ((w' << 4) & 0xF0F0F0F0) 16 q of the even ones, and each byte
+// converts exactly in one sign-extending instruction (11 VALU instructions
+// per 8 codes), then one f32 FMA per code and token; the power of two 16 is
+// taken out together with the group scale.  The lane sums of 16 row steps
+// are reduced together by a lane-transposed butterfly (one DPP level per
+// lane bit) instead of one full DPP reduction per row.
 //
 // Every size a buffer descriptor or a scalar offset is built from comes from
 // the host (F32Mat), so descriptors and row offsets stay in scalar registers.
@@ -40,7 +41,6 @@ namespace qmoe {
 
 constexpr int F32_GU_ROWS = 32;     // gate (and up) rows per gate+up block
 constexpr int F32_DN_STEPS = 16;    // row steps per down wave
-constexpr int F32_U = 4;            // row steps per load batch
 constexpr int F32_MAX_WAVES = 8;
 
 // The pass of a block, in LDS: expert, token count and per token the row of
@@ -155,16 +155,21 @@ __device__ void plan_wave(const F32Route &r, int a, const int *sid, PassLds *pl)
     }
 }
 
-// Stage the plan of this block into LDS (inline mode stages the ids first)
-// and return its token count (0: nothing to do; uniform over the block).
+// Stage the plan of this block into LDS and return its token count (0:
+// nothing to do; uniform over the block).  Inline mode with several tokens per
+// pass stages the ids and lets one wave search the partners; otherwise every
+// wave plans for itself from global memory (all write the same values), which
+// keeps the block's barriers off the path to its first weight loads.
 template <int TB>
 __device__ __forceinline__ int stage_plan(const F32Route &r, int a, int *sid, PassLds *pl) {
-    if (r.ids) {
+    if (r.ids && TB > 1) {
         for (int i = threadIdx.x; i < r.n; i += blockDim.x) sid[i] = r.ids[i];
         __syncthreads();
+        if (wave_id() == 0) plan_wave<TB>(r, a, sid, pl);
+        __syncthreads();
+    } else {
+        plan_wave<TB>(r, a, r.ids, pl);
     }
-    if (wave_id() == 0) plan_wave<TB>(r, a, sid, pl);
-    __syncthreads();
     return __builtin_amdgcn_readfirstlane(pl->nt);
 }
 
@@ -235,72 +240,129 @@ __device__ __forceinline__ void chunk_fma(const u32x4 &w, const float (&x)[TB][3
     }
 }
 
+// Lane-transposed sum of 2^D row steps (a butterfly over lane bits 0..D-1).
+// Step values arrive one at a time; level b combines two partial sums that
+// each cover 2^b steps: every lane adds its value to the partner's (lane bit b
+// flipped: quad_perm for bits 0 and 1, a rotation by 4 or 8 inside the DPP row
+// for bits 2 and 3, which keeps the lower bits) and keeps the half of the
+// steps whose bit b equals its own lane bit b.  After all D levels lane l
+// holds a partial sum for step l mod 2^D; the lanes of an L-lane row that hold
+// the same step (they differ only in bits D and up) cover disjoint lane sets
+// whose union is the whole row, so their partial sums add up to the row sum.
+// Every level costs one output per 2^(b+1) steps, three VALU instructions
+// each (two DPP adds and a bit select).
+template <int D>
+struct Butterfly {
+    float v[D + 1];   // v[b]: the pending partial sum that covers 2^b steps
+};
+template <int CTRL>
+__device__ __forceinline__ float dpp_sum(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// Level B of the butterfly for a value of batch step `step`; false when the
+// value waits for its partner block (the push ends there).
+template <int B, int D>
+__device__ __forceinline__ bool butterfly_level(Butterfly<D> &bf, float &v, int step) {
+    if constexpr (B < D) {
+        if (((step >> B) & 1) == 0) {
+            bf.v[B] = v;
+            return false;
+        }
+        constexpr int ctrl = B == 0 ? 0xB1 : B == 1 ? 0x4E : B == 2 ? 0x124 : 0x128;
+        const float lo = dpp_sum<ctrl>(bf.v[B]), hi = dpp_sum<ctrl>(v);
+        // lane bit B ? hi : lo, as a bit select (truth table 0xD8 = c ? b : a)
+        const uint32_t m = 0u - (uint32_t)((lane_id() >> B) & 1);
+        v = __uint_as_float(__builtin_amdgcn_bitop3_b32(__float_as_uint(lo), __float_as_uint(hi), m, 0xD8));
+    }
+    return true;
+}
+// Push the value of batch step `step` (compile-time after unrolling); returns
+// the lane's finished sum after the batch's last step.
+template <int D>
+__device__ __forceinline__ float butterfly_push(Butterfly<D> &bf, float v, int step) {
+    if (!butterfly_level<0, D>(bf, v, step)) return 0.f;
+    if (!butterfly_level<1, D>(bf, v, step)) return 0.f;
+    if (!butterfly_level<2, D>(bf, v, step)) return 0.f;
+    if (!butterfly_level<3, D>(bf, v, step)) return 0.f;
+    return v;
+}
+
+// Butterfly depth of a stream of NST steps, and the parts (lane groups whose
+// partial sums are added in the epilogue) per row: L >> depth.
+static inline int f32_depth_rt(int nst) { return nst >= 16 ? 4 : nst >= 8 ? 3 : nst >= 4 ? 2 : 1; }
+template <int NST>
+constexpr int f32_depth() { return NST >= 16 ? 4 : NST >= 8 ? 3 : NST >= 4 ? 2 : 1; }
+template <int L, int NST>
+constexpr int f32_parts() { return L >> f32_depth<NST>(); }
+
+// Load steps in flight per wave, per tokens per pass.
+template <int TB>
+constexpr int f32_prefetch() { return TB == 1 ? 12 : TB == 2 ? 8 : 4; }
+
 // Stream NST row steps of one slice: step j reads row row0 + j*(64/L) + the
-// lane's sub-row (the last row of the matrix past its end), in batches of
-// F32_U steps with the next batch's loads issued before the current batch is
-// computed.  The L-lane sum of step j, token t lands in
-// red[t * ld + j * (64/L) + sub-row].
-template <int L, int TB, int NT, int NST>
+// lane's sub-row (the last row of the matrix past its end).  Loads run PD
+// steps ahead.  Each step's chunk sums, times the lane's group scale, go
+// through a butterfly of depth D (2^D steps); lane l then writes, for step
+// 2^D * batch + (l mod 2^D), its partial row sum to
+// red[t * ld_t + part * ld_p + step * (64/L) + sub-row], part = (l mod L) >> D.
+template <int L, int TB, int NT, int NST, int PD>
 __device__ __forceinline__ void stream_slice(const SliceSrc &src, uint32_t rb, uint32_t sb,
                                              int row0, int rows, const float (&x)[TB][32],
-                                             float *red, int ld) {
+                                             float *red, int ld_t, int ld_p) {
     constexpr int RPI = QMOE_WAVE / L;
-    constexpr int NB = NST / F32_U;
-    static_assert(NB * F32_U == NST, "steps must be a multiple of the batch");
+    constexpr int D = f32_depth<NST>();
+    constexpr int BD = 1 << D;
+    static_assert(NST % BD == 0, "steps must be a multiple of the butterfly batch");
     const int lane = lane_id();
     const int sr = lane / L;
-    u32x4 wq[2][F32_U];
-    float ws[2][F32_U];
-    auto load = [&](int b, int slot) {
-#pragma unroll
-        for (int u = 0; u < F32_U; u++) {
-            const int j = b * F32_U + u;
-            if (RPI == 1) {
-                // one row per wave instruction: the row offset is scalar
-                const int row = min(row0 + j, rows - 1);
-                wq[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane,
-                                                                    (uint32_t)row * rb, 0);
-                ws[slot][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    src.s, src.slane, (uint32_t)row * sb, 0));
-            } else {
-                const int row = min(row0 + j * RPI + sr, rows - 1);
-                wq[slot][u] = __builtin_amdgcn_raw_buffer_load_b128(
-                    src.q, src.qlane + (uint32_t)row * rb, 0u, 0);
-                ws[slot][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    src.s, src.slane + (uint32_t)row * sb, 0u, 0));
-            }
+    u32x4 wq[PD];
+    float ws[PD];
+    auto load = [&](int j) {
+        if (RPI == 1) {
+            // one row per wave instruction: the row offset is scalar
+            const int row = min(row0 + j, rows - 1);
+            wq[j % PD] = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane, (uint32_t)row * rb, 0);
+            ws[j % PD] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(src.s, src.slane, (uint32_t)row * sb, 0));
+        } else {
+            const int row = min(row0 + j * RPI + sr, rows - 1);
+            wq[j % PD] = __builtin_amdgcn_raw_buffer_load_b128(src.q, src.qlane + (uint32_t)row * rb, 0u, 0);
+            ws[j % PD] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(src.s, src.slane + (uint32_t)row * sb, 0u, 0));
         }
     };
-    load(0, 0);
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-        if (b + 1 < NB) load(b + 1, (b + 1) & 1);
+    for (int j = 0; j < PD && j < NST; j++) load(j);
+    Butterfly<D> bf[NT];
+    float *dst = red + ((lane % L) >> D) * ld_p + (lane & (BD - 1)) * RPI + sr;
 #pragma unroll
-        for (int u = 0; u < F32_U; u++) {
-            float acc[TB];
-            chunk_fma<TB, NT>(wq[b & 1][u], x, acc);
+    for (int j = 0; j < NST; j++) {
+        float acc[TB];
+        chunk_fma<TB, NT>(wq[j % PD], x, acc);
+        const float sc = ws[j % PD] * 0.0625f;
+        if (j + PD < NST) load(j + PD);
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const float v = reduce_dpp<L>(acc[t] * ws[b & 1][u]);
-                if ((lane % L) == L - 1) red[t * ld + (b * F32_U + u) * RPI + sr] = v;
-            }
+        for (int t = 0; t < NT; t++) {
+            const float v = butterfly_push<D>(bf[t], acc[t] * sc, j % BD);
+            if (j % BD == BD - 1) dst[t * ld_t + (j / BD) * BD * RPI] = v;
         }
     }
 }
 
 // The NT-token instance of a slice stream, chosen by the pass's token count.
-template <int L, int TB, int NST>
+template <int L, int TB, int NST, int PD>
 __device__ __forceinline__ void stream_slice_nt(int nt, const SliceSrc &src, uint32_t rb,
                                                 uint32_t sb, int row0, int rows,
-                                                const float (&x)[TB][32], float *red, int ld) {
+                                                const float (&x)[TB][32], float *red, int ld_t,
+                                                int ld_p) {
     if (TB >= 4 && nt == 4)
-        stream_slice<L, TB, (TB >= 4 ? 4 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+        stream_slice<L, TB, (TB >= 4 ? 4 : 1), NST, PD>(src, rb, sb, row0, rows, x, red, ld_t, ld_p);
     else if (TB >= 3 && nt == 3)
-        stream_slice<L, TB, (TB >= 3 ? 3 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+        stream_slice<L, TB, (TB >= 3 ? 3 : 1), NST, PD>(src, rb, sb, row0, rows, x, red, ld_t, ld_p);
     else if (TB >= 2 && nt == 2)
-        stream_slice<L, TB, (TB >= 2 ? 2 : 1), NST>(src, rb, sb, row0, rows, x, red, ld);
+        stream_slice<L, TB, (TB >= 2 ? 2 : 1), NST, PD>(src, rb, sb, row0, rows, x, red, ld_t, ld_p);
     else
-        stream_slice<L, TB, 1, NST>(src, rb, sb, row0, rows, x, red, ld);
+        stream_slice<L, TB, 1, NST, PD>(src, rb, sb, row0, rows, x, red, ld_t, ld_p);
 }
 
 // Blocks per SIMD the register allocation targets, per tokens per pass (no
@@ -341,7 +403,8 @@ __device__ __forceinline__ F32Lds f32_lds(float *base, int nred) {
 // ---------------------------------------------------------------------------
 // gate+up: block = (32 rows of F, one pass).  Waves 0..S-1 stream the gate
 // slices, waves S..2S-1 the same rows of up; the epilogue writes
-// h = silu(g) * u in f32 for the pass's tokens, row hrow of h.
+// h = silu(g) * u in f32 for the pass's tokens, row hrow of h.  Cross-slice
+// sums: red[(((m * S + s) * TB + t) * P + part) * 32 + row], P parts per row.
 // ---------------------------------------------------------------------------
 template <int L, int TB>
 __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
@@ -351,6 +414,7 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     extern __shared__ float lds_gu[];
     constexpr int RPI = QMOE_WAVE / L;
     constexpr int NST = F32_GU_ROWS / RPI;
+    constexpr int P = f32_parts<L, NST>();
     int a = f32_slot();
     if (r.lead_row) {
         if (a == 0) {
@@ -359,7 +423,7 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
         }
         a -= 1;
     }
-    const int nred = 2 * S * TB * F32_GU_ROWS;
+    const int nred = 2 * S * TB * P * F32_GU_ROWS;
     const F32Lds l = f32_lds(lds_gu, nred);
     const int nt = stage_plan<TB>(r, a, l.sid, l.pl);
     if (nt == 0) return;
@@ -375,8 +439,9 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     for (int t = 0; t < TB; t++)
         if (t < nt) load_chunk(xr[t], x, l.pl->tok[t], H, chunk * 32, H, true);
     const int row0 = blockIdx.x * F32_GU_ROWS;
-    float *red = l.red + (m * S + s) * TB * F32_GU_ROWS;
-    stream_slice_nt<L, TB, NST>(nt, src, M.rb, M.sb, row0, F, xr, red, F32_GU_ROWS);
+    float *red = l.red + (m * S + s) * TB * P * F32_GU_ROWS;
+    stream_slice_nt<L, TB, NST, f32_prefetch<TB>()>(nt, src, M.rb, M.sb, row0, F, xr, red,
+                                                    P * F32_GU_ROWS, F32_GU_ROWS);
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid < nt * F32_GU_ROWS) {
@@ -384,12 +449,11 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
         const int f = row0 + rr;
         if (f < F) {
             float g = 0.f, u = 0.f;
-            for (int k = 0; k < S; k++) {
-                g += l.red[(k * TB + t) * F32_GU_ROWS + rr];
-                u += l.red[((S + k) * TB + t) * F32_GU_ROWS + rr];
+            for (int k = 0; k < S * P; k++) {
+                const int sk = k / P, pk = k % P;
+                g += l.red[((sk * TB + t) * P + pk) * F32_GU_ROWS + rr];
+                u += l.red[(((S + sk) * TB + t) * P + pk) * F32_GU_ROWS + rr];
             }
-            g *= 0.0625f;
-            u *= 0.0625f;
             h[(int64_t)l.pl->hrow[t] * F + f] = silu(g) * u;
         }
     }
@@ -399,6 +463,7 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
 // down (and the plain matvec): block = (R * 16 * 64/L output rows, one pass);
 // wave w streams slice w % S of row group w / S.  Routed: out[tok] += w * y
 // with f32 atomics (out was cleared ahead of the launch); direct: out = y.
+// Cross-slice sums: red[((s * TB + t) * P + part) * NR + row].
 // ---------------------------------------------------------------------------
 template <int L, int TB>
 __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
@@ -408,8 +473,9 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     extern __shared__ float lds_dn[];
     constexpr int RPI = QMOE_WAVE / L;
     constexpr int RW = F32_DN_STEPS * RPI;     // rows per row group
+    constexpr int P = f32_parts<L, F32_DN_STEPS>();
     const int NR = R * RW;
-    const F32Lds l = f32_lds(lds_dn, S * TB * NR);
+    const F32Lds l = f32_lds(lds_dn, S * TB * P * NR);
     const int nt = stage_plan<TB>(r, f32_slot(), l.sid, l.pl);
     if (nt == 0) return;
     const int e = __builtin_amdgcn_readfirstlane(l.pl->e);
@@ -423,16 +489,16 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     for (int t = 0; t < TB; t++)
         if (t < nt) load_chunk(xr[t], hin, l.pl->hrow[t], h_ld, chunk * 32, h_cols, vec);
     const int row0 = blockIdx.x * NR;
-    float *red = l.red + s * TB * NR + rg * RW;
-    stream_slice_nt<L, TB, F32_DN_STEPS>(nt, src, D.rb, D.sb, row0 + rg * RW, O, xr, red, NR);
+    float *red = l.red + s * TB * P * NR + rg * RW;
+    stream_slice_nt<L, TB, F32_DN_STEPS, f32_prefetch<TB>()>(nt, src, D.rb, D.sb, row0 + rg * RW,
+                                                             O, xr, red, P * NR, NR);
     __syncthreads();
     for (int i = threadIdx.x; i < nt * NR; i += blockDim.x) {
         const int t = i / NR, rr = i % NR;
         const int o = row0 + rr;
         if (o >= O) continue;
         float y = 0.f;
-        for (int k = 0; k < S; k++) y += l.red[(k * TB + t) * NR + rr];
-        y *= 0.0625f;
+        for (int k = 0; k < S * P; k++) y += l.red[(((k / P) * TB + t) * P + k % P) * NR + rr];
         float *dst = out + (int64_t)l.pl->tok[t] * O + o;
         if (routed) unsafeAtomicAdd(dst, l.pl->w[t] * y);
         else *dst = y;
@@ -533,7 +599,8 @@ hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, f
     if (!sh.L || (r.ids && r.n > F32_INLINE_MAX)) return hipErrorInvalidValue;
     const dim3 grid = f32_grid((gate.rows + F32_GU_ROWS - 1) / F32_GU_ROWS, f32_slots(r, tb));
     const dim3 block(2 * sh.S * QMOE_WAVE);
-    const size_t lds = f32_lds_bytes(r, (size_t)2 * sh.S * tb * F32_GU_ROWS);
+    const int P = sh.L >> f32_depth_rt(F32_GU_ROWS * sh.L / QMOE_WAVE);
+    const size_t lds = f32_lds_bytes(r, (size_t)2 * sh.S * tb * P * F32_GU_ROWS);
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
 #define X(L_, T_)                                                                              \
     if (sh.L == L_ && tb == T_) {                                                              \
@@ -555,7 +622,8 @@ hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int
     const int NR = R * F32_DN_STEPS * (QMOE_WAVE / sh.L);
     const dim3 grid = f32_grid((down.rows + NR - 1) / NR, f32_slots(r, tb));
     const dim3 block(sh.S * R * QMOE_WAVE);
-    const size_t lds = f32_lds_bytes(r, (size_t)sh.S * tb * NR);
+    const int P = sh.L >> f32_depth_rt(F32_DN_STEPS);
+    const size_t lds = f32_lds_bytes(r, (size_t)sh.S * tb * P * NR);
     const bool vec = h_cols % 4 == 0 && h_ld % 4 == 0 &&
                      (reinterpret_cast<uintptr_t>(hin) & 15u) == 0;
     const F32Mat D = f32_mat(down);
