@@ -572,68 +572,103 @@ PCIE_PEAK = 64.0e9     # B/s, host link of one MI355X (PCIe 5.0 x16, one directi
 
 
 def time_host_experts(qm, synth, torch, dev, layer, slots=32, calls=16, reps=3):
-    """Decode (1 token, top-8) with all 128 experts in pinned host memory and
-    `slots` expert slots in HBM (qmoe_cache_prepare copies the routed experts
-    that are missing, then the layer runs on the slots).  Timed two ways:
-    serial (copies and kernels on one stream) and pipelined (the copies of
-    call i+1 on a second stream overlap the kernels of call i).  Roofline:
-    the bytes copied over the host link at PCIE_PEAK.  Not part of the step."""
+    """Decode with all 128 experts in pinned host memory and `slots` expert
+    slots in HBM.  Two routings: one token with uniform logits (every call
+    needs about 8 new experts: bound by the host link) and 4 tokens with
+    Zipf(1.1) expert popularity over 64 slots (most experts hit, so copies
+    and kernels are of comparable length).  Modes: host prepare
+    (qmoe_cache_prepare from host ids, DMA copies) serial and pipelined (the
+    copies of call i+1 on a second stream overlap the kernels of call i), and
+    device prepare (qmoe_cache_prepare_device from device ids: the slots are
+    chosen and filled by GPU kernels, no host round trip) serial and
+    pipelined.  Roofline: the bytes copied over the host link at PCIE_PEAK.
+    Not part of the step."""
     pin = lambda t: t.cpu().pin_memory()
     t = layer.tensors
     host = qm.HostLayer(*[pin(x) for x in t], H, F)
-    dev_t = [torch.empty((slots,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev) for x in t]
-    slot_layer = qm.QLayer(*dev_t, H, F)
-    wl = synth.LAYERS["decode_e128_t1"]
-    gen = synth.generator(wl.seed + 2000)
-    inputs = [synth.layer_inputs(wl, gen) for _ in range(calls)]
-    xs = [x.to(dev) for x, _, _ in inputs]
-    ws = [w.to(dev) for _, _, w in inputs]
-    ids_h = [ids.contiguous() for _, ids, _ in inputs]
-    slot_h = [torch.empty(1, K, dtype=torch.int32).pin_memory() for _ in range(calls)]
-    slot_d = [torch.empty(1, K, dtype=torch.int32, device=dev) for _ in range(calls)]
-    outs = [torch.empty(1, H, device=dev) for _ in range(calls)]
-    wsp = torch.empty(slot_layer.workspace_bytes(1, K, qm.QMOE_F32), dtype=torch.uint8,
-                      device=dev)
     comp = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
     res = {}
-    for mode in ("serial", "pipelined"):
-        best = None
-        for _ in range(reps):
-            cache = qm.ExpertCache(host, slot_layer)       # cold: every call starts empty
-            done = [torch.cuda.Event() for _ in range(calls)]
-            ready = [torch.cuda.Event() for _ in range(calls)]
-            nbytes = 0
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(comp)
-            t0 = time.perf_counter()
+    cases = (("uniform_t1", synth.LAYERS["decode_e128_t1"], slots),
+             ("zipf_t4", synth.Workload("zipf_t4", E, H, F, K, 4, "f32", "zipf", 4), 64))
+    for cname, wl, nslots in cases:
+        dev_t = [torch.empty((nslots,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+                 for x in t]
+        slot_layer = qm.QLayer(*dev_t, H, F)
+        T = wl.tokens
+        gen = synth.generator(wl.seed + 2000)
+        inputs = [synth.layer_inputs(wl, gen) for _ in range(calls)]
+        xs = [x.to(dev) for x, _, _ in inputs]
+        ws = [w.to(dev) for _, _, w in inputs]
+        ids_h = [ids.contiguous() for _, ids, _ in inputs]
+        ids_d = [ids.to(dev) for ids in ids_h]
+        slot_h = [torch.empty(T, K, dtype=torch.int32).pin_memory() for _ in range(calls)]
+        slot_d = [torch.empty(T, K, dtype=torch.int32, device=dev) for _ in range(calls)]
+        outs = [torch.empty(T, H, device=dev) for _ in range(calls)]
+        wsp = torch.empty(slot_layer.workspace_bytes(T, K, qm.QMOE_F32), dtype=torch.uint8,
+                          device=dev)
+        res[cname] = {}
+        for mode in ("serial", "pipelined", "device_serial", "device_pipelined"):
+            best = None
+            for _ in range(reps):
+                cache = qm.ExpertCache(host, slot_layer)   # cold: every run starts empty
+                state = cache.device_state(stream=comp) if mode.startswith("device") else None
+                done = [torch.cuda.Event() for _ in range(calls)]
+                ready = [torch.cuda.Event() for _ in range(calls)]
+                ncopy = torch.zeros(calls, dtype=torch.int32, device=dev)
+                nbytes = 0
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(comp)
+                for i in range(calls):
+                    st = comp if mode.endswith("serial") else copy
+                    if st is copy and i >= 2:
+                        copy.wait_event(done[i - 2])         # call i-2's slots may go now
+                    if state is None:
+                        _, nb = cache.prepare(ids_h[i], slot_ids=slot_h[i], stream=st)
+                        nbytes += nb
+                        with torch.cuda.stream(st):
+                            slot_d[i].copy_(slot_h[i], non_blocking=True)
+                    else:
+                        cache.prepare_device(state, ids_d[i], slot_ids=slot_d[i], stream=st)
+                        with torch.cuda.stream(st):
+                            ncopy[i].copy_(state[2])          # experts this call copied
+                    ready[i].record(st)
+                    comp.wait_event(ready[i])
+                    qm.qmoe_layer(slot_layer, xs[i], slot_d[i], ws[i], out=outs[i], ws=wsp,
+                                  stream=comp)
+                    done[i].record(comp)
+                b.record(comp)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b)
+                if state is not None:
+                    # the device decided what to copy: its per-call counts
+                    assert int(state[1].item()) == 0, "device cache overflow"
+                    nbytes = int(ncopy.sum().item()) * EXPERT_BYTES
+                cache.close()
+                if best is None or ms < best[0]:
+                    best = (ms, nbytes)
+            ms, nbytes = best
+            res[cname][mode] = {"us_per_call": round(ms * 1e3 / calls, 1),
+                                "host_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                                "frac_of_pcie_roofline": round(nbytes / PCIE_PEAK / (ms * 1e-3), 4),
+                                "bytes_copied": nbytes}
+        # the layer alone on the slots (slot ids of the last run): the kernel
+        # time a pipelined run can hide under the copies
+        def layers():
             for i in range(calls):
-                st = comp if mode == "serial" else copy
-                if mode == "pipelined" and i >= 2:
-                    copy.wait_event(done[i - 2])             # call i-2's slots may go now
-                _, nb = cache.prepare(ids_h[i], slot_ids=slot_h[i], stream=st)
-                nbytes += nb
-                with torch.cuda.stream(st):
-                    slot_d[i].copy_(slot_h[i], non_blocking=True)
-                ready[i].record(st)
-                comp.wait_event(ready[i])
-                qm.qmoe_layer(slot_layer, xs[i], slot_d[i], ws[i], out=outs[i], ws=wsp,
-                              stream=comp)
-                done[i].record(comp)
-            b.record(comp)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b)
-            cache.close()
-            if best is None or ms < best[0]:
-                best = (ms, nbytes)
-        ms, nbytes = best
-        res[mode] = {"us_per_call": round(ms * 1e3 / calls, 1),
-                     "host_GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                     "frac_of_pcie_roofline": round(nbytes / PCIE_PEAK / (ms * 1e-3), 4),
-                     "bytes_copied": nbytes}
-    res["config"] = {"experts_in_host_memory": E, "hbm_slots": slots, "tokens": 1, "topk": K,
-                     "calls": calls, "pcie_peak_GBps": PCIE_PEAK / 1e9}
+                qm.qmoe_layer(slot_layer, xs[i], slot_d[i], ws[i], out=outs[i], ws=wsp)
+        lay_us = time_graph(torch, layers, reps) * 1e3 / calls
+        for host_or_dev in ("", "device_"):
+            ser = res[cname][host_or_dev + "serial"]["us_per_call"]
+            pip = res[cname][host_or_dev + "pipelined"]["us_per_call"]
+            res[cname][host_or_dev + "overlap"] = {
+                "layer_only_us_per_call": round(lay_us, 1),
+                "saved_us_per_call": round(ser - pip, 1),
+                "fraction_of_layer_hidden": round((ser - pip) / lay_us, 3)}
+        res[cname]["config"] = {"experts_in_host_memory": E, "hbm_slots": nslots, "tokens": T,
+                                "topk": K, "calls": calls, "routing": wl.logits}
+    res["pcie_peak_GBps"] = PCIE_PEAK / 1e9
     return res
 
 

@@ -62,7 +62,8 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_worklist_workspace_bytes", "qmoe_worklist", "qmoe_layer_workspace_bytes",
            "qmoe_layer", "qmoe_layer_ex", "qmoe_layer_ws_layout", "qmoe_route",
            "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
-           "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_layer_logits_workspace_bytes",
+           "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_cache_device_state_bytes",
+           "qmoe_cache_device_init", "qmoe_cache_prepare_device", "qmoe_layer_logits_workspace_bytes",
            "qmoe_layer_logits", "qmoe_layer_noalloc"]
 
 _lib = None
@@ -110,6 +111,9 @@ def load(path: str | None = None):
         "qmoe_cache_destroy": (None, [vp]),
         "qmoe_cache_prepare": (ctypes.c_int, [vp, vp, i32, i32, vp, ctypes.POINTER(i64), vp]),
         "qmoe_cache_resident": (i32, [vp, i32]),
+        "qmoe_cache_device_state_bytes": (sz, [i32, i32]),
+        "qmoe_cache_device_init": (ctypes.c_int, [vp, vp, sz, vp]),
+        "qmoe_cache_prepare_device": (ctypes.c_int, [vp, vp, sz, vp, i32, i32, vp, vp]),
         "qmoe_layer_logits_workspace_bytes": (sz, [ctypes.POINTER(qmoe_layer_desc), i32, i32, i32]),
         "qmoe_layer_logits": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp, i32,
                                              vp, vp, sz, vp]),
@@ -301,6 +305,29 @@ class ExpertCache:
 
     def resident(self, expert):
         return int(self._lib.qmoe_cache_resident(self.handle, expert))
+
+    def device_state(self, stream=None):
+        """A fresh device state for prepare_device (int32 device tensor),
+        initialised on `stream` to an empty cache."""
+        nb = int(self._lib.qmoe_cache_device_state_bytes(self.host.experts,
+                                                         self.slots.desc.experts))
+        st = torch.empty(nb // 4, dtype=torch.int32, device=self.slots.tensors[0].device)
+        _check(self._lib.qmoe_cache_device_init(self.handle, _ptr(st), nb, _stream(stream)),
+               "qmoe_cache_device_init")
+        return st
+
+    def prepare_device(self, state, dev_ids, slot_ids=None, stream=None):
+        """dev_ids int32 device [T, k] -> slot_ids int32 device [T, k]; the
+        missing experts are chosen and copied on the device (no host sync)."""
+        _dev(dev_ids, "dev_ids", torch.int32)
+        T, k = dev_ids.shape
+        out = slot_ids if slot_ids is not None else torch.empty(T, k, dtype=torch.int32,
+                                                                device=dev_ids.device)
+        _check(self._lib.qmoe_cache_prepare_device(self.handle, _ptr(state), state.numel() * 4,
+                                                   _ptr(dev_ids), T, k, _ptr(out),
+                                                   _stream(stream)),
+               "qmoe_cache_prepare_device")
+        return out
 
     def close(self):
         if self.handle:

@@ -263,6 +263,45 @@ int qmoe_cache_prepare(qmoe_expert_cache *cache, const int32_t *host_ids, int32_
 /* Slot holding `expert`, or -1 (not resident or out of range). */
 int32_t qmoe_cache_resident(const qmoe_expert_cache *cache, int32_t expert);
 
+/* Device-side prepare: the same cache, deciding on the device from device
+ * routing ids (as the router writes them), with no host round trip
+ * (pxq_llama.cpp release notes, "Device-side MoE row map": the device builds
+ * the map, no device-to-host sync).
+ *
+ * qmoe_cache_device_state_bytes: bytes of the caller-owned device state for
+ * E experts and S slots (int32 words: tick, status, copy count, unused,
+ * slot_of[E], expert_in[S], last_use[S], keep[S], copy list 2 x [S]); 0 for
+ * E or S < 1.
+ *
+ * qmoe_cache_device_init: enqueue on `stream` the state of an empty cache
+ * (no expert resident).  QMOE_ERR_UNSUPPORTED beyond 8192 experts or 1024
+ * slots, QMOE_ERR_WORKSPACE when state_bytes is too small, QMOE_ERR_ALIGN
+ * for a state not 4-byte aligned.
+ *
+ * qmoe_cache_prepare_device: for the device routing ids of one call (int32
+ * [tokens][k]) enqueue on `stream` one kernel that keeps the resident experts,
+ * gives each missing valid expert a slot (free slots first, then the least
+ * recently used slot that neither this call nor the previous prepare uses;
+ * missing experts are placed in ascending id order), updates the state and
+ * writes dev_slot_ids (device int32 [tokens][k]: the slot of each pair, -1
+ * for ids outside [0, E)), then a kernel that copies the placed experts' six
+ * arrays from the host layer into their slots.  The host arrays must be
+ * pinned host memory (QMOE_ERR_UNSUPPORTED otherwise); the GPU reads them
+ * directly.  Stream rules are those of qmoe_cache_prepare: call i+1's prepare
+ * may overlap call i's layer kernels, call i+2's must wait for them.  When a
+ * call's experts plus the previous call's other slots exceed S, the experts
+ * that found no slot keep slot id -1 (their pairs add nothing) and status
+ * word 1 of the state becomes 1 (the device cannot report it synchronously;
+ * read it back to check).  The state must come from qmoe_cache_device_init
+ * on this cache's shape; do not mix it with qmoe_cache_prepare on one cache
+ * (the two keep separate residency tables). */
+size_t qmoe_cache_device_state_bytes(int32_t experts, int32_t slots);
+int qmoe_cache_device_init(qmoe_expert_cache *cache, void *dev_state, size_t state_bytes,
+                           void *stream);
+int qmoe_cache_prepare_device(qmoe_expert_cache *cache, void *dev_state, size_t state_bytes,
+                              const int32_t *dev_ids, int32_t tokens, int32_t k,
+                              int32_t *dev_slot_ids, void *stream);
+
 /* Router, the step ahead of the layer: for each token, the k experts with
  * the largest logits and their routing weights (colibri pull request
  * "cuda+engine: full fmt=4 (grouped int4 gs=64) support", the quoted issue's

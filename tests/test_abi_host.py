@@ -244,6 +244,35 @@ def test_cache_create_validation(lib):
     assert lib.qmoe_cache_create(None, ctypes.byref(dev), ctypes.byref(h)) == 1
 
 
+def test_cache_device_validation(lib):
+    host, dev = layer_desc(E=16), layer_desc(E=4)
+    h = ctypes.c_void_p()
+    assert lib.qmoe_cache_create(ctypes.byref(host), ctypes.byref(dev), ctypes.byref(h)) == 0
+    nb = lib.qmoe_cache_device_state_bytes(16, 4)
+    assert nb == 4 * (4 + 16 + 5 * 4)
+    assert lib.qmoe_cache_device_state_bytes(0, 4) == 0
+    assert lib.qmoe_cache_device_state_bytes(16, 0) == 0
+    # rejections happen before anything is enqueued
+    assert lib.qmoe_cache_device_init(None, FAKE, nb, None) == 1
+    assert lib.qmoe_cache_device_init(h, None, nb, None) == 1
+    assert lib.qmoe_cache_device_init(h, FAKE, nb - 4, None) == 5
+    assert lib.qmoe_cache_device_init(h, FAKE + 2, nb, None) == 3
+    assert lib.qmoe_cache_prepare_device(h, FAKE, nb, None, 2, 2, None, None) == 1
+    assert lib.qmoe_cache_prepare_device(h, FAKE, nb, FAKE, 2, 0, FAKE, None) == 2
+    assert lib.qmoe_cache_prepare_device(h, FAKE, nb, FAKE, -1, 2, FAKE, None) == 2
+    assert lib.qmoe_cache_prepare_device(h, FAKE, nb - 4, FAKE, 2, 2, FAKE, None) == 5
+    assert lib.qmoe_cache_prepare_device(h, None, nb, FAKE, 2, 2, FAKE, None) == 1
+    lib.qmoe_cache_destroy(h)
+    # more slots than the device tables hold
+    big = layer_desc(E=2000)
+    assert lib.qmoe_cache_create(ctypes.byref(layer_desc(E=3000)), ctypes.byref(big),
+                                 ctypes.byref(h)) == 0
+    nb = lib.qmoe_cache_device_state_bytes(3000, 2000)
+    assert lib.qmoe_cache_device_init(h, FAKE, nb, None) == 4
+    assert lib.qmoe_cache_prepare_device(h, FAKE, nb, FAKE, 2, 2, FAKE, None) == 4
+    lib.qmoe_cache_destroy(h)
+
+
 def test_layer_logits_validation(lib):
     d = layer_desc()
     T, k = 2, 2
