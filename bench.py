@@ -334,6 +334,19 @@ def time_decode_phases(qm, torch, decode_dev, gu_bytes_by_t):
     return res
 
 
+def time_matvec(qm, torch, q, s, x, y, ws, calls=64, reps=3):
+    """The 256 x 1024 matvec alone: `calls` calls in a graph (the 148 KB of
+    weights stay in L2 after the first, so this is its launch-bound latency).
+    Not part of the step."""
+    def run():
+        for _ in range(calls):
+            qm.qmoe_matvec(q, s, MATVEC[1], x, out=y, ws=ws)
+    best = time_graph(torch, run, reps)
+    nbytes = MATVEC[0] * MATVEC[1] // 2 + MATVEC[0] * MATVEC[1] // 64 * 4 + MATVEC[1] * 8
+    return {"workload": "matvec_256x1024 (batch 1, f32)", "us_per_call": round(best * 1e3 / calls, 2),
+            "alg_bytes": nbytes, "GBps": round(nbytes / (best * 1e-3 / calls) / 1e9, 1)}
+
+
 def time_expert_ffn(qm, synth, torch, dev, copies=64, reps=3):
     """The single expert (hidden 4096, intermediate 1536, f32 x [1 x 4096]):
     one qmoe_expert_ffn call per copy of the expert's weights, `copies`
@@ -928,6 +941,7 @@ def main():
             "by_tokens": time_decode_by_tokens(qm, torch, decode_dev, bytes_by_t,
                                                x_dtype=qm.QMOE_F32_DIGITS)}
         log("single expert ...")
+        rec["matvec"] = time_matvec(qm, torch, mq_d, ms_d, mx_d, my_d, mws)
         rec["expert_ffn"] = time_expert_ffn(qm, synth, torch, dev)
         log("256-expert Zipf layer ...")
         rec["layer_e256_zipf"] = time_layer_e256(qm, synth, torch, dev)

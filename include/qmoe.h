@@ -394,9 +394,9 @@ int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens,
  * Nothing is allocated or freed and nothing in the array needs to start at
  * zero.  A call whose qmoe_layer_workspace_bytes exceeds the array returns
  * QMOE_ERR_SCRATCH and launches nothing (at hidden 4096, intermediate 1536
- * and top-8, the 64 MiB hold the f32 path up to about 1,500 tokens and the
- * bf16 path up to about 650 tokens).  Every
- * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * and top-8, the 64 MiB hold the f32 path up to 1,354 tokens, the digits
+ * variant up to 1,546 and the bf16 path up to 668 tokens).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one
  * GPU (different streams, or different host threads without ordering) race
  * and give wrong results; calls serialised on one stream are safe.  After a
  * call the array begins with the worklist in the layout of
