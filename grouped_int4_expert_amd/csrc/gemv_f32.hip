@@ -39,8 +39,11 @@
 
 namespace qmoe {
 
-constexpr int F32_GU_ROWS = 32;     // gate (and up) rows per gate+up block
-constexpr int F32_DN_STEPS = 16;    // row steps per down wave
+// Rows per gate+up block and row steps per down wave: the long form, and a
+// short form for launches with few passes (more, shorter waves: the one-token
+// layer and the single expert are latency-bound).
+constexpr int F32_GU_ROWS = 32, F32_GU_ROWS_SHORT = 8;
+constexpr int F32_DN_STEPS = 16, F32_DN_STEPS_SHORT = 4;
 constexpr int F32_MAX_WAVES = 8;
 
 // The pass of a block, in LDS: expert, token count and per token the row of
@@ -401,19 +404,19 @@ __device__ __forceinline__ F32Lds f32_lds(float *base, int nred) {
 }
 
 // ---------------------------------------------------------------------------
-// gate+up: block = (32 rows of F, one pass).  Waves 0..S-1 stream the gate
+// gate+up: block = (ROWS rows of F, one pass).  Waves 0..S-1 stream the gate
 // slices, waves S..2S-1 the same rows of up; the epilogue writes
 // h = silu(g) * u in f32 for the pass's tokens, row hrow of h.  Cross-slice
-// sums: red[(((m * S + s) * TB + t) * P + part) * 32 + row], P parts per row.
+// sums: red[(((m * S + s) * TB + t) * P + part) * ROWS + row], P parts per row.
 // ---------------------------------------------------------------------------
-template <int L, int TB>
+template <int L, int TB, int ROWS>
 __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     __attribute__((amdgpu_waves_per_eu(f32_waves_per_eu<TB>())))
     f32_gateup_kernel(F32Mat G, F32Mat Up, const float *__restrict__ x, float *__restrict__ h,
                       F32Route r, int S) {
     extern __shared__ float lds_gu[];
     constexpr int RPI = QMOE_WAVE / L;
-    constexpr int NST = F32_GU_ROWS / RPI;
+    constexpr int NST = ROWS / RPI;
     constexpr int P = f32_parts<L, NST>();
     int a = f32_slot();
     if (r.lead_row) {
@@ -423,7 +426,7 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
         }
         a -= 1;
     }
-    const int nred = 2 * S * TB * P * F32_GU_ROWS;
+    const int nred = 2 * S * TB * P * ROWS;
     const F32Lds l = f32_lds(lds_gu, nred);
     const int nt = stage_plan<TB>(r, a, l.sid, l.pl);
     if (nt == 0) return;
@@ -438,21 +441,21 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
 #pragma unroll
     for (int t = 0; t < TB; t++)
         if (t < nt) load_chunk(xr[t], x, l.pl->tok[t], H, chunk * 32, H, true);
-    const int row0 = blockIdx.x * F32_GU_ROWS;
-    float *red = l.red + (m * S + s) * TB * P * F32_GU_ROWS;
+    const int row0 = blockIdx.x * ROWS;
+    float *red = l.red + (m * S + s) * TB * P * ROWS;
     stream_slice_nt<L, TB, NST, f32_prefetch<TB>()>(nt, src, M.rb, M.sb, row0, F, xr, red,
-                                                    P * F32_GU_ROWS, F32_GU_ROWS);
+                                                    P * ROWS, ROWS);
     __syncthreads();
     const int tid = threadIdx.x;
-    if (tid < nt * F32_GU_ROWS) {
-        const int t = tid / F32_GU_ROWS, rr = tid % F32_GU_ROWS;
+    if (tid < nt * ROWS) {
+        const int t = tid / ROWS, rr = tid % ROWS;
         const int f = row0 + rr;
         if (f < F) {
             float g = 0.f, u = 0.f;
             for (int k = 0; k < S * P; k++) {
                 const int sk = k / P, pk = k % P;
-                g += l.red[((sk * TB + t) * P + pk) * F32_GU_ROWS + rr];
-                u += l.red[(((S + sk) * TB + t) * P + pk) * F32_GU_ROWS + rr];
+                g += l.red[((sk * TB + t) * P + pk) * ROWS + rr];
+                u += l.red[(((S + sk) * TB + t) * P + pk) * ROWS + rr];
             }
             h[(int64_t)l.pl->hrow[t] * F + f] = silu(g) * u;
         }
@@ -460,20 +463,20 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
 }
 
 // ---------------------------------------------------------------------------
-// down (and the plain matvec): block = (R * 16 * 64/L output rows, one pass);
+// down (and the plain matvec): block = (R * STEPS * 64/L output rows, one pass);
 // wave w streams slice w % S of row group w / S.  Routed: out[tok] += w * y
 // with f32 atomics (out was cleared ahead of the launch); direct: out = y.
 // Cross-slice sums: red[((s * TB + t) * P + part) * NR + row].
 // ---------------------------------------------------------------------------
-template <int L, int TB>
+template <int L, int TB, int STEPS>
 __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
     __attribute__((amdgpu_waves_per_eu(f32_waves_per_eu<TB>())))
     f32_down_kernel(F32Mat D, const float *__restrict__ hin, int64_t h_ld, int h_cols,
                     float *__restrict__ out, F32Route r, int S, int R, bool routed, bool vec) {
     extern __shared__ float lds_dn[];
     constexpr int RPI = QMOE_WAVE / L;
-    constexpr int RW = F32_DN_STEPS * RPI;     // rows per row group
-    constexpr int P = f32_parts<L, F32_DN_STEPS>();
+    constexpr int RW = STEPS * RPI;     // rows per row group
+    constexpr int P = f32_parts<L, STEPS>();
     const int NR = R * RW;
     const F32Lds l = f32_lds(lds_dn, S * TB * P * NR);
     const int nt = stage_plan<TB>(r, f32_slot(), l.sid, l.pl);
@@ -490,7 +493,7 @@ __global__ void __launch_bounds__(F32_MAX_WAVES * QMOE_WAVE)
         if (t < nt) load_chunk(xr[t], hin, l.pl->hrow[t], h_ld, chunk * 32, h_cols, vec);
     const int row0 = blockIdx.x * NR;
     float *red = l.red + s * TB * P * NR + rg * RW;
-    stream_slice_nt<L, TB, F32_DN_STEPS, f32_prefetch<TB>()>(nt, src, D.rb, D.sb, row0 + rg * RW,
+    stream_slice_nt<L, TB, STEPS, f32_prefetch<TB>()>(nt, src, D.rb, D.sb, row0 + rg * RW,
                                                              O, xr, red, P * NR, NR);
     __syncthreads();
     for (int i = threadIdx.x; i < nt * NR; i += blockDim.x) {
@@ -593,22 +596,38 @@ static size_t f32_lds_bytes(const F32Route &r, size_t nred) {
     return b;
 }
 
+// Waves a launch would have at the long block forms; below this, the short
+// forms (4x the blocks, a quarter of the rows each).  Only one-token passes
+// take them (larger passes run at 2 waves per SIMD and are not latency-bound).
+constexpr int64_t F32_SHORT_BELOW = 2048;
+static int64_t f32_est_passes(const F32Route &r, int tb) {
+    if (r.ids) return r.n;
+    if (r.rec) return r.max_rec;
+    return (r.ntok + tb - 1) / tb;
+}
+
 hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, float *h,
                              const F32Route &r, int tb, hipStream_t st) {
     const F32Shape sh = f32_shape(gate.cols, F32_MAX_WAVES / 2);
     if (!sh.L || (r.ids && r.n > F32_INLINE_MAX)) return hipErrorInvalidValue;
-    const dim3 grid = f32_grid((gate.rows + F32_GU_ROWS - 1) / F32_GU_ROWS, f32_slots(r, tb));
+    const int64_t waves_long = (int64_t)2 * sh.S * ((gate.rows + F32_GU_ROWS - 1) / F32_GU_ROWS) *
+                               f32_est_passes(r, tb);
+    const int rows = (tb == 1 && waves_long < F32_SHORT_BELOW) ? F32_GU_ROWS_SHORT : F32_GU_ROWS;
+    const dim3 grid = f32_grid((gate.rows + rows - 1) / rows, f32_slots(r, tb));
     const dim3 block(2 * sh.S * QMOE_WAVE);
-    const int P = sh.L >> f32_depth_rt(F32_GU_ROWS * sh.L / QMOE_WAVE);
-    const size_t lds = f32_lds_bytes(r, (size_t)2 * sh.S * tb * P * F32_GU_ROWS);
+    const int P = sh.L >> f32_depth_rt(rows * sh.L / QMOE_WAVE);
+    const size_t lds = f32_lds_bytes(r, (size_t)2 * sh.S * tb * P * rows);
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
-#define X(L_, T_)                                                                              \
-    if (sh.L == L_ && tb == T_) {                                                              \
-        hipLaunchKernelGGL((f32_gateup_kernel<L_, T_>), grid, block, lds, st, G, U, x, h, r,   \
-                           sh.S);                                                              \
+#define X(L_, T_, R_)                                                                          \
+    if (sh.L == L_ && tb == T_ && rows == R_) {                                                \
+        hipLaunchKernelGGL((f32_gateup_kernel<L_, T_, R_>), grid, block, lds, st, G, U, x, h,   \
+                           r, sh.S);                                                           \
         return hipGetLastError();                                                              \
     }
-    X(64, 1) X(64, 2) X(64, 4) X(32, 1) X(32, 2) X(32, 4) X(16, 1) X(16, 2) X(16, 4)
+    X(64, 1, F32_GU_ROWS) X(64, 2, F32_GU_ROWS) X(64, 4, F32_GU_ROWS)
+    X(32, 1, F32_GU_ROWS) X(32, 2, F32_GU_ROWS) X(32, 4, F32_GU_ROWS)
+    X(16, 1, F32_GU_ROWS) X(16, 2, F32_GU_ROWS) X(16, 4, F32_GU_ROWS)
+    X(64, 1, F32_GU_ROWS_SHORT) X(32, 1, F32_GU_ROWS_SHORT) X(16, 1, F32_GU_ROWS_SHORT)
 #undef X
     return hipErrorInvalidValue;
 }
@@ -619,21 +638,29 @@ hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int
     if (!sh.L || (r.ids && r.n > F32_INLINE_MAX) || r.lead_row) return hipErrorInvalidValue;
     int R = 4 / sh.S;
     if (R < 1) R = 1;
-    const int NR = R * F32_DN_STEPS * (QMOE_WAVE / sh.L);
+    const int rpi = QMOE_WAVE / sh.L;
+    const int nr_long = R * F32_DN_STEPS * rpi;
+    const int64_t waves_long = (int64_t)sh.S * R * ((down.rows + nr_long - 1) / nr_long) *
+                               f32_est_passes(r, tb);
+    const int steps = (tb == 1 && waves_long < F32_SHORT_BELOW) ? F32_DN_STEPS_SHORT : F32_DN_STEPS;
+    const int NR = R * steps * rpi;
     const dim3 grid = f32_grid((down.rows + NR - 1) / NR, f32_slots(r, tb));
     const dim3 block(sh.S * R * QMOE_WAVE);
-    const int P = sh.L >> f32_depth_rt(F32_DN_STEPS);
+    const int P = sh.L >> f32_depth_rt(steps);
     const size_t lds = f32_lds_bytes(r, (size_t)sh.S * tb * P * NR);
     const bool vec = h_cols % 4 == 0 && h_ld % 4 == 0 &&
                      (reinterpret_cast<uintptr_t>(hin) & 15u) == 0;
     const F32Mat D = f32_mat(down);
-#define X(L_, T_)                                                                              \
-    if (sh.L == L_ && tb == T_) {                                                              \
-        hipLaunchKernelGGL((f32_down_kernel<L_, T_>), grid, block, lds, st, D, hin, h_ld,       \
+#define X(L_, T_, S_)                                                                          \
+    if (sh.L == L_ && tb == T_ && steps == S_) {                                               \
+        hipLaunchKernelGGL((f32_down_kernel<L_, T_, S_>), grid, block, lds, st, D, hin, h_ld,   \
                            h_cols, out, r, sh.S, R, routed, vec);                              \
         return hipGetLastError();                                                              \
     }
-    X(64, 1) X(64, 2) X(64, 4) X(32, 1) X(32, 2) X(32, 4) X(16, 1) X(16, 2) X(16, 4)
+    X(64, 1, F32_DN_STEPS) X(64, 2, F32_DN_STEPS) X(64, 4, F32_DN_STEPS)
+    X(32, 1, F32_DN_STEPS) X(32, 2, F32_DN_STEPS) X(32, 4, F32_DN_STEPS)
+    X(16, 1, F32_DN_STEPS) X(16, 2, F32_DN_STEPS) X(16, 4, F32_DN_STEPS)
+    X(64, 1, F32_DN_STEPS_SHORT) X(32, 1, F32_DN_STEPS_SHORT) X(16, 1, F32_DN_STEPS_SHORT)
 #undef X
     return hipErrorInvalidValue;
 }
