@@ -131,7 +131,7 @@ hipError_t launch_gemv_matvec(const QMat &w, XDigits xd, int batch, float *y,
 // plan records over sorted positions from the preparation kernel) or direct
 // (neither: expert 0, slot a = tokens a*tb ..).  The rows of h are pairs
 // (inline), sorted positions (record) or tokens (direct).
-constexpr int F32_INLINE_MAX = 1024;
+constexpr int F32_INLINE_MAX = 64;
 struct F32Route {
     const int32_t *ids;     // inline: topk ids [n]
     const float *topk_w;    // inline: routing weights [n]

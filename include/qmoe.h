@@ -335,8 +335,10 @@ size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
  * paths an expert's tokens are taken one, two or four per weight pass; the
  * passes of one expert run side by side, so its weights come from HBM about
  * once per call and the later passes read them from the L2 cache.  With
- * QMOE_F32 and at most 1024 pairs (tokens * k) the call is two kernel
- * launches (gate+up, which also groups the pairs by expert, then down).
+ * QMOE_F32 and at most 64 pairs (tokens * k) the call is two kernel launches
+ * (gate+up, which also groups the pairs by expert, then down); beyond that a
+ * preparation kernel plans the passes once (three launches: faster from 128
+ * pairs on, where every gate+up block would otherwise scan all the ids).
  * Reproducibility: the bf16 path sums each token's k expert rows in pick
  * order and gives bit-identical results from run to run; the f32 paths add
  * the k expert terms into out with f32 atomics, so their order, and the
@@ -362,7 +364,7 @@ int qmoe_layer_logits(const qmoe_layer_desc *desc, int32_t x_dtype, const void *
  * n_events hipEvent_t handles (passed as void*, created by the caller) and the
  * call records events[0] before its first kernel and events[i] after phase i
  * on `stream`.  Phases: f32 paths 1 = worklist (+ activation digits for
- * QMOE_F32_DIGITS; for QMOE_F32 with at most 1024 pairs the gate+up launch
+ * QMOE_F32_DIGITS; for QMOE_F32 with at most 64 pairs the gate+up launch
  * builds the worklist itself and phase 1 is empty), 2 = gate+up, 3 = down and
  * combine (n_events >= 4); bf16 path 1 = worklist + activation prep,
  * 2 = gate+up, 3 = down, 4 = combine (n_events >= 5).  Fewer events =

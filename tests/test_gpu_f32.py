@@ -1,8 +1,8 @@
 """The f32 decode path (QMOE_F32: every code unpacked to f32, f32 FMA chains,
 f32 group scale) and its digit variant (QMOE_F32_DIGITS), against the oracle:
 activations whose 64-element groups span a large dynamic range, NaN and
-infinity in x, the pass grouping of the two-launch call at and past its
-1024-pair limit, and the digit variant selected explicitly."""
+infinity in x, the pass grouping of the two-launch call (at most 64 pairs)
+and of the planned call past it, and the digit variant selected explicitly."""
 import numpy as np
 import pytest
 import torch
@@ -106,11 +106,11 @@ def test_layer_nan_reaches_its_token_only(code):
     check(out[keep], ref[keep], None, path, "other tokens")
 
 
-@pytest.mark.parametrize("T", [128, 129])
+@pytest.mark.parametrize("T", [8, 9, 128, 129])
 def test_layer_inline_limit(T):
-    """T x 8 = 1024 pairs: two launches, the pass grouping derived inside the
-    gate+up blocks; 1032 pairs: the preparation kernel's plan records.  16
-    experts, so most experts have many pairs (four tokens per pass)."""
+    """T x 8 = 64 pairs: two launches, the pass grouping derived inside the
+    gate+up blocks; 72 pairs and more: the preparation kernel's plan records.
+    16 experts, so most experts have several pairs (four tokens per pass)."""
     say(f"layer f32 E=16 H=256 F=128 T={T} k=8")
     L = Layer(16, 256, 128, seed=507)
     g = synth.generator(508 + T)
@@ -136,6 +136,27 @@ def test_layer_pass_grouping(counts_e):
     assign = torch.repeat_interleave(torch.arange(len(counts)), torch.tensor(counts) * 2)[perm]
     ids = (assign * (E // 16)).to(torch.int32).view(T, 2)
     g = synth.generator(510)
+    x = synth.rand_x(g, (T, 192))
+    w = torch.rand((T, 2), generator=g)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
+
+
+@pytest.mark.parametrize("counts_e", [8, 48, 1024])
+def test_layer_pass_grouping_inline(counts_e):
+    """At most 64 pairs (the gate+up launch groups them itself): experts with
+    1..7 pairs at expert counts that select four, two and one tokens per
+    weight pass."""
+    counts = [1, 2, 3, 4, 5, 6, 7]
+    T = sum(counts)
+    E = counts_e
+    say(f"layer f32 E={E} H=192 F=320 T={T} k=2 (inline), fixed pairs per expert")
+    L = Layer(E, 192, 320, seed=513)
+    perm = torch.randperm(2 * T, generator=torch.Generator().manual_seed(513))
+    assign = torch.repeat_interleave(torch.arange(len(counts)), torch.tensor(counts) * 2)[perm]
+    ids = (assign * (E // 8)).to(torch.int32).view(T, 2)
+    g = synth.generator(514)
     x = synth.rand_x(g, (T, 192))
     w = torch.rand((T, 2), generator=g)
     out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
