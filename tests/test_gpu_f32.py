@@ -123,10 +123,11 @@ def test_layer_inline_limit(T):
     check(out, ref, mag, "f32", "layer")
 
 
-@pytest.mark.parametrize("counts_e", [16, 48, 1024])
+@pytest.mark.parametrize("counts_e", [16, 64, 128, 1024])
 def test_layer_pass_grouping(counts_e):
-    """Experts with 1..17 pairs (duplicates in one token included) at expert
-    counts that select four, two and one tokens per weight pass."""
+    """Experts with 1..17 pairs (duplicates in one token included; 206 pairs,
+    past the inline limit) at expert counts that select four tokens per pass
+    in both launches, four in gate+up and two in down, two in both, and one."""
     counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 16, 17]
     T = sum(counts)
     E = counts_e
