@@ -476,6 +476,40 @@ def test_layer_graph_replays_match_eager(dtype):
         assert rel_l2(out.cpu().numpy(), eager.cpu().numpy()) <= 1e-6, rep
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_side_stream_internal_workspace(dtype):
+    """A call on a side stream with no workspace argument: the binding's
+    internal workspace must not be handed out again on the current stream
+    while the side stream's kernels still use it.  The side stream is kept
+    busy first, so the layer's kernels run well after the call returns; the
+    current stream then allocates the same size and overwrites it."""
+    say(f"side-stream layer with internal workspace {dtype}")
+    L = Layer(16, 256, 128, seed=35)
+    g = synth.generator(36)
+    wl = synth.Workload("t", 16, 256, 128, 4, 33, dtype, "normal", 36)
+    x, ids, w = synth.layer_inputs(wl, g)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), w.to(DEV)
+    code = qm.QMOE_F32 if dtype == "f32" else qm.QMOE_BF16
+    ref = qm.qmoe_layer(L.dev, xd, idd, wd)
+    torch.cuda.synchronize()
+    nb = L.dev.workspace_bytes(33, 4, code)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = torch.empty_like(ref)
+    a = torch.full((2048, 2048), 1.0 / 2048, device=DEV)
+    with torch.cuda.stream(side):
+        b = a
+        for _ in range(24):
+            b = torch.mm(b, a)             # keeps the side stream busy
+    qm.qmoe_layer(L.dev, xd, idd, wd, out=out, stream=side)
+    junk = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    junk.fill_(0xAB)
+    torch.cuda.synchronize()
+    del b
+    assert torch.isfinite(out).all()
+    assert rel_l2(out.cpu().numpy(), ref.cpu().numpy()) <= 1e-6
+
+
 @pytest.mark.parametrize("rows,cols,offset", [(5, 4096, 0), (7, 33, 0), (3, 1000, 3), (1, 1, 0)])
 def test_import_twos(rows, cols, offset):
     say(f"import two's complement rows={rows} cols={cols} offset={offset}")
