@@ -39,11 +39,13 @@
 
 namespace qmoe {
 
-// Rows per gate+up block and row steps per down wave: the long form, and a
-// short form for launches with few passes (more, shorter waves: the one-token
-// layer and the single expert are latency-bound).
-constexpr int F32_GU_ROWS = 32, F32_GU_ROWS_SHORT = 8;
-constexpr int F32_DN_STEPS = 16, F32_DN_STEPS_SHORT = 4;
+// Rows per gate+up block and row steps per down wave, chosen per launch from
+// the waves the launch would have at 32 rows / 16 steps: small launches (the
+// single expert, the one-token layer) are latency-bound and take more,
+// shorter waves; passes of several tokens take longer down waves (fewer block
+// set-ups for the same weights).
+constexpr int F32_GU_ROWS = 32, F32_GU_ROWS_MID = 16, F32_GU_ROWS_SHORT = 8;
+constexpr int F32_DN_STEPS_LONG = 32, F32_DN_STEPS = 16, F32_DN_STEPS_SHORT = 4;
 constexpr int F32_MAX_WAVES = 8;
 
 // The pass of a block, in LDS: expert, token count and per token the row of
@@ -598,10 +600,11 @@ static size_t f32_lds_bytes(const F32Route &r, size_t nred) {
     return b;
 }
 
-// Waves a launch would have at the long block forms; below this, the short
-// forms (4x the blocks, a quarter of the rows each).  Only one-token passes
-// take them (larger passes run at 2 waves per SIMD and are not latency-bound).
-constexpr int64_t F32_SHORT_BELOW = 2048;
+// Measured per call (one-token passes): the single expert 16.8 us at 32 rows,
+// 11.5 at 8; the one-token layer 29-31 us at 32 or 8 rows, 28 at 16; the
+// four-token layer is best at 32 rows.  Down at 32 steps for multi-token
+// passes: the 64-token Zipf layer's down 430 -> 389 us.
+constexpr int64_t F32_SHORT_BELOW = 512, F32_MID_BELOW = 2048;
 static int64_t f32_est_passes(const F32Route &r, int tb) {
     if (r.ids) return r.n;
     if (r.rec) return r.max_rec;
@@ -614,7 +617,10 @@ hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, f
     if (!sh.L || (r.ids && r.n > F32_INLINE_MAX)) return hipErrorInvalidValue;
     const int64_t waves_long = (int64_t)2 * sh.S * ((gate.rows + F32_GU_ROWS - 1) / F32_GU_ROWS) *
                                f32_est_passes(r, tb);
-    const int rows = (tb == 1 && waves_long < F32_SHORT_BELOW) ? F32_GU_ROWS_SHORT : F32_GU_ROWS;
+    const int rows = tb > 1 ? F32_GU_ROWS
+                     : waves_long < F32_SHORT_BELOW ? F32_GU_ROWS_SHORT
+                     : waves_long < F32_MID_BELOW   ? F32_GU_ROWS_MID
+                                                    : F32_GU_ROWS;
     const dim3 grid = f32_grid((gate.rows + rows - 1) / rows, f32_slots(r, tb));
     const dim3 block(2 * sh.S * QMOE_WAVE);
     const int P = sh.L >> f32_depth_rt(rows * sh.L / QMOE_WAVE);
@@ -630,6 +636,7 @@ hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, f
     X(32, 1, F32_GU_ROWS) X(32, 2, F32_GU_ROWS) X(32, 4, F32_GU_ROWS)
     X(16, 1, F32_GU_ROWS) X(16, 2, F32_GU_ROWS) X(16, 4, F32_GU_ROWS)
     X(64, 1, F32_GU_ROWS_SHORT) X(32, 1, F32_GU_ROWS_SHORT) X(16, 1, F32_GU_ROWS_SHORT)
+    X(64, 1, F32_GU_ROWS_MID) X(32, 1, F32_GU_ROWS_MID) X(16, 1, F32_GU_ROWS_MID)
 #undef X
     return hipErrorInvalidValue;
 }
@@ -644,7 +651,9 @@ hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int
     const int nr_long = R * F32_DN_STEPS * rpi;
     const int64_t waves_long = (int64_t)sh.S * R * ((down.rows + nr_long - 1) / nr_long) *
                                f32_est_passes(r, tb);
-    const int steps = (tb == 1 && waves_long < F32_SHORT_BELOW) ? F32_DN_STEPS_SHORT : F32_DN_STEPS;
+    const int steps = tb > 1 ? F32_DN_STEPS_LONG
+                      : waves_long < F32_MID_BELOW ? F32_DN_STEPS_SHORT
+                                                   : F32_DN_STEPS;
     const int NR = R * steps * rpi;
     const dim3 grid = f32_grid((down.rows + NR - 1) / NR, f32_slots(r, tb));
     const dim3 block(sh.S * R * QMOE_WAVE);
@@ -659,9 +668,9 @@ hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int
                            h_cols, out, r, sh.S, R, routed, vec);                              \
         return hipGetLastError();                                                              \
     }
-    X(64, 1, F32_DN_STEPS) X(64, 2, F32_DN_STEPS) X(64, 4, F32_DN_STEPS)
-    X(32, 1, F32_DN_STEPS) X(32, 2, F32_DN_STEPS) X(32, 4, F32_DN_STEPS)
-    X(16, 1, F32_DN_STEPS) X(16, 2, F32_DN_STEPS) X(16, 4, F32_DN_STEPS)
+    X(64, 1, F32_DN_STEPS) X(64, 2, F32_DN_STEPS_LONG) X(64, 4, F32_DN_STEPS_LONG)
+    X(32, 1, F32_DN_STEPS) X(32, 2, F32_DN_STEPS_LONG) X(32, 4, F32_DN_STEPS_LONG)
+    X(16, 1, F32_DN_STEPS) X(16, 2, F32_DN_STEPS_LONG) X(16, 4, F32_DN_STEPS_LONG)
     X(64, 1, F32_DN_STEPS_SHORT) X(32, 1, F32_DN_STEPS_SHORT) X(16, 1, F32_DN_STEPS_SHORT)
 #undef X
     return hipErrorInvalidValue;
