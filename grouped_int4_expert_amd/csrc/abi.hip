@@ -124,6 +124,7 @@ struct LayerWs {
     XDigits xd, hd;
     DecodePlan plan;
     float *hf;           // f32 path: h [pairs][F]
+    XSplit xs;           // f32 path, matrix-core record mode: f16 parts of x
     uint16_t *x16, *h16;
     float *xinv;
     YBuf y;
@@ -156,6 +157,10 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
             L.plan.tok = c.take<int32_t>(n);
             L.plan.wsort = c.take<float>(n);
             L.plan.max_rec = (int)n;
+            if (H % 256 == 0 && xsplit_bytes(T, H) < ((int64_t)1 << 31)) {
+                L.xs.v = c.take<uint16_t>(xsplit_bytes(T, H) / 2);
+                L.xs.f = c.take<float>(T);
+            }
         }
         L.hf = c.take<float>(n * F);
     } else if (dtype == QMOE_F32_DIGITS) {
@@ -593,8 +598,11 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
     hipError_t e = mark();
     if (e != hipSuccess) return QMOE_ERR_HIP;
     if (x_dtype == QMOE_F32) {
-        const int tb_gu = f32_tokens_per_pass((int)n, E, true);
-        const int tb_dn = f32_tokens_per_pass((int)n, E, false);
+        // record mode runs the passes on the matrix cores where the shapes allow
+        const bool mf_gu = n > F32_INLINE_MAX && L.xs.v && mfd_gateup_supported(G, U);
+        const bool mf_dn = n > F32_INLINE_MAX && mfd_down_supported(D);
+        const int tb_gu = mf_gu ? MFD_TB : f32_tokens_per_pass((int)n, E, true);
+        const int tb_dn = mf_dn ? MFD_TB : f32_tokens_per_pass((int)n, E, false);
         F32Route r{};
         r.k = k;
         r.E = E;
@@ -618,19 +626,31 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
             plan.tb_gu = tb_gu;
             plan.tb_dn = tb_dn;
             e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, plan,
-                                   static_cast<const float *>(x), tokens, H, XDigits{}, out, st);
+                                   static_cast<const float *>(x), tokens, H, XDigits{},
+                                   mf_gu ? L.xs : XSplit{}, out, st);
             if (e == hipSuccess) e = mark();
             r.rec = plan.rec_gu;
             r.tok = plan.tok;
             r.wsort = plan.wsort;
             r.max_rec = plan.max_rec;
         }
-        if (e == hipSuccess)
-            e = launch_f32_gateup(G, U, static_cast<const float *>(x), L.hf, r, tb_gu, st);
+        if (e == hipSuccess) {
+            if (mf_gu)
+                e = launch_mfd_gateup(G, U, L.xs, tokens, L.hf, L.plan.rec_gu, L.plan.tok,
+                                      L.plan.max_rec, st);
+            else
+                e = launch_f32_gateup(G, U, static_cast<const float *>(x), L.hf, r, tb_gu, st);
+        }
         if (e == hipSuccess) e = mark();
         r.lead_row = 0;
         if (r.rec) r.rec = L.plan.rec_dn;
-        if (e == hipSuccess) e = launch_f32_down(D, L.hf, F, F, out, r, tb_dn, true, st);
+        if (e == hipSuccess) {
+            if (mf_dn)
+                e = launch_mfd_down(D, L.hf, out, L.plan.rec_dn, L.plan.tok, L.plan.wsort,
+                                    L.plan.max_rec, st);
+            else
+                e = launch_f32_down(D, L.hf, F, F, out, r, tb_dn, true, st);
+        }
         if (e == hipSuccess) e = mark();
     } else if (x_dtype == QMOE_F32_DIGITS) {
         Worklist wl = L.wl;
@@ -640,7 +660,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         plan.tb_gu = gemv_tokens_per_pass(G, (int)n, E, true);
         plan.tb_dn = gemv_tokens_per_pass(D, (int)n, E, false);
         e = launch_decode_prep(topk_ids, topk_w, (int)n, k, E, wl, plan,
-                               static_cast<const float *>(x), tokens, H, L.xd, out, st);
+                               static_cast<const float *>(x), tokens, H, L.xd, XSplit{}, out,
+                               st);
         if (e == hipSuccess) e = mark();
         GemvRoute r{};
         r.rec = plan.rec_gu;

@@ -1,0 +1,373 @@
+// Decode GEMVs of the routed layer on the matrix cores, in f32 arithmetic.
+//
+// What is computed is the same as the f32 GEMVs of gemv_f32.hip (per-group
+// f32 scale applied once per 64-input group, f32 accumulation; colibri pull
+// request "cuda+engine: full fmt=4 (grouped int4 gs=64) support", Summary and
+// comment "blocked by GPU driver instability"), for passes of up to four
+// tokens of one expert.  The f32 activations are carried as three exact f16
+// parts each (split16.h), the codes as exact f16 q - 8, and
+// v_mfma_f32_16x16x32_f16 forms the products exactly and adds them in f32.
+// Where the VALU kernels spend one f32 FMA per code and token on top of the
+// unpack, here the code-times-token work moves to the matrix cores and the
+// vector ALUs only unpack, so a pass of several tokens costs about what one
+// token does.
+//
+// MFMA roles.  A operand (16 rows m): m = 4 t + p, token t of the pass
+// (0..3), part p (0..2; p = 3 is zero).  B operand (16 columns): 16 weight
+// rows.  D: lane l holds the four parts of token l / 16 for weight row
+// l % 16, so a lane needs one scale per group and sums its own parts at the
+// end.  Per 128-input load step a lane reads 16 packed bytes of its row
+// (lane group l / 16 at byte 16 (l / 16)), two dwords swap lane halves
+// (split16.h), and four MFMAs follow: steps 0 and 1 accumulate the first
+// 64-input group, steps 2 and 3 the second; each group's partial sums are
+// multiplied by the row's f32 scale and added to the f32 totals.
+//
+// gate+up reads the activation parts from the preparation kernel's split of
+// x (global memory, L2-resident); down splits its pass's h rows itself into
+// LDS, one split per block shared by its waves.  Records, rows of h and the
+// routed atomic adds into out are those of the record mode of the VALU
+// kernels.
+#include "common.h"
+#include "launch.h"
+#include "split16.h"
+
+namespace qmoe {
+
+// A block = one pass x MFD_R 16-row blocks x the whole input width: wave w
+// takes inputs 512 w .. 512 w + 511 (four load steps), so its activation
+// operands (64 registers) are read once; it streams its R row blocks, each
+// as four back-to-back loads of 64 bytes per row (256 contiguous bytes), and
+// leaves one partial sum per row and token in LDS; the block adds the
+// slices' partials at the end.  gate+up: row blocks 0..R/2-1 of gate and the
+// same rows of up.
+constexpr int MFD_R = 16;          // 16-row blocks per block
+constexpr int MFD_KW = 512;        // inputs per wave
+constexpr int MFD_LPW = MFD_KW / SP_STEP;
+constexpr int MFD_GU_WAVES = 12;   // gate+up inputs up to 6144
+constexpr int MFD_DN_WAVES = MFD_DOWN_MAX_COLS / MFD_KW;
+constexpr int MFD_STAGES = 2;      // row blocks in flight per wave
+
+struct MfdPass {
+    int e, p0, nt;
+};
+
+// Record `slot` of the plan (expert, first and end sorted position).
+__device__ __forceinline__ MfdPass mfd_pass(const int32_t *rec, int slot) {
+    MfdPass p;
+    p.e = __builtin_amdgcn_readfirstlane(rec[4 * slot]);
+    p.p0 = __builtin_amdgcn_readfirstlane(rec[4 * slot + 1]);
+    const int end = __builtin_amdgcn_readfirstlane(rec[4 * slot + 2]);
+    p.nt = min(end - p.p0, MFD_TB);
+    return p;
+}
+
+// One expert's matrix as the main loop reads it: descriptors over its codes
+// and scales, lane offsets of row lane % 16 at this wave's first input, the
+// byte stride of 16 rows.
+struct MfdMat {
+    __amdgpu_buffer_rsrc_t q, s;
+    uint32_t qlane, slane;     // per lane
+    uint32_t qwave, swave;     // this wave's slice (uniform)
+    uint32_t q16, s16;         // 16 rows
+    int gshift;
+};
+
+__device__ __forceinline__ MfdMat mfd_mat(const F32Mat &M, int e, int row0, int w) {
+    MfdMat m;
+    const int lane = lane_id();
+    m.q = make_rsrc(M.q + (int64_t)e * M.q_stride, M.qbytes);
+    m.s = make_rsrc(M.s + (int64_t)e * M.s_stride, M.sbytes);
+    m.qlane = (uint32_t)(lane & 15) * M.rb + 16u * (uint32_t)(lane >> 4);
+    m.slane = (uint32_t)(lane & 15) * M.sb;
+    m.qwave = (uint32_t)row0 * M.rb + (uint32_t)(MFD_KW / 2) * (uint32_t)w;
+    m.swave = (uint32_t)row0 * M.sb;
+    m.q16 = 16u * M.rb;
+    m.s16 = 16u * M.sb;
+    m.gshift = M.gshift;
+    return m;
+}
+
+// Main loop of one wave: a[L][i] = activation operands of its four load
+// steps; rows blocks b = 0..R-1 of matrix M0 (b < R0) or M1 (b >= R0, row
+// block b - R0); `part(b, y)` receives the lane's part sum of row block b.
+// Input k0 of the wave: MFD_KW * w.  G64: group 64 (scales of the slice are
+// 8 consecutive floats per row).  `ready()` runs once the first row blocks'
+// loads are issued, before `a` is read (it may fill `a`).
+template <int R, int R0, bool G64, typename Part, typename Ready>
+__device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const MfdMat &M0,
+                                             const MfdMat &M1, int w, Part part, Ready ready) {
+    u32x4 wq[MFD_STAGES][MFD_LPW];
+    float sc[MFD_STAGES][2 * MFD_LPW];
+    // loads of row block b into stage st: the four load steps of each row
+    // back to back, then the slice's scales
+    auto issue = [&](int b, int st) {
+        __builtin_amdgcn_sched_barrier(0);
+        const MfdMat &M = b < R0 ? M0 : M1;
+        const int bb = b < R0 ? b : b - R0;
+        const uint32_t qo = M.qwave + (uint32_t)bb * M.q16;
+#pragma unroll
+        for (int L = 0; L < MFD_LPW; L++)
+            wq[st][L] = __builtin_amdgcn_raw_buffer_load_b128(M.q, M.qlane, qo + 64u * L, 0);
+        const uint32_t so = M.swave + (uint32_t)bb * M.s16;
+        if constexpr (G64) {
+            const uint32_t g0 = (uint32_t)(2 * MFD_LPW) * (uint32_t)w * 4u;
+#pragma unroll
+            for (int v = 0; v < 2 * MFD_LPW / 4; v++) {
+                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(M.s, M.slane, so + g0 + 16u * v, 0);
+#pragma unroll
+                for (int c = 0; c < 4; c++) sc[st][4 * v + c] = __uint_as_float(t[c]);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2 * MFD_LPW; h++) {
+                const uint32_t gi = ((uint32_t)(MFD_KW * w + 64 * h) >> M.gshift) * 4u;
+                sc[st][h] = __uint_as_float(
+                    __builtin_amdgcn_raw_buffer_load_b32(M.s, M.slane, so + gi, 0));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](int b, int st) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        f32x4 tot = zero;
+#pragma unroll
+        for (int L = 0; L < MFD_LPW; L++) {
+            const u32x4 q = wq[st][L];
+            // lanes 32..63 of dwords 0, 1 <-> lanes 0..31 of dwords 2, 3
+            const auto s02 = __builtin_amdgcn_permlane32_swap(q[0], q[2], false, false);
+            const auto s13 = __builtin_amdgcn_permlane32_swap(q[1], q[3], false, false);
+            const f16x8 b0 = sp_codes8(s02[0]), b1 = sp_codes8(s13[0]);
+            const f16x8 b2 = sp_codes8(s02[1]), b3 = sp_codes8(s13[1]);
+            f32x4 pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][0], b0, zero, 0, 0, 0);
+            pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][1], b1, pa, 0, 0, 0);
+            f32x4 pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][2], b2, zero, 0, 0, 0);
+            pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][3], b3, pb, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                tot[v] = fmaf(sc[st][2 * L], pa[v], fmaf(sc[st][2 * L + 1], pb[v], tot[v]));
+        }
+        // parts of the lane's token (register 3 is the zero part), smallest first
+        part(b, (tot[2] + tot[1]) + tot[0]);
+    };
+#pragma unroll
+    for (int b = 0; b < MFD_STAGES && b < R; b++) issue(b, b);
+    ready();
+#pragma unroll
+    for (int b = 0; b < R; b++) {
+        compute(b, b % MFD_STAGES);
+        if (b + MFD_STAGES < R) issue(b + MFD_STAGES, b % MFD_STAGES);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gate+up: block = one pass x 8 row blocks (128 rows) of gate and of up;
+// h[p0 + t][f] = silu(g) * u.
+// ---------------------------------------------------------------------------
+template <bool G64>
+__global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
+    F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h,
+    const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp, int max_rec) {
+    extern __shared__ float part_lds[];   // [S][R][64]
+    const int slot = blockIdx.z * gridDim.y + blockIdx.y;
+    if (slot >= max_rec) return;
+    const MfdPass ps = mfd_pass(rec, slot);
+    if (ps.e < 0 || ps.nt <= 0) return;
+    const int F = G.rows, NL = G.cols / SP_STEP, S = G.cols / MFD_KW;
+    const int row0 = blockIdx.x * (16 * MFD_R / 2);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int lane = lane_id(), n = lane & 15;
+    // activation operands: A row m = n is token n / 4, part n % 4 (part 3 and
+    // missing tokens read past the descriptor: zero)
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(xs.v, xs_bytes);
+    uint32_t aoff = OOB_OFFSET;
+    const int ta = n >> 2, pa = n & 3;
+    if (ta < ps.nt && pa < SP_PARTS) {
+        const int tok = tokp[ps.p0 + ta];
+        aoff = (uint32_t)(((int64_t)tok * NL * 48 + (lane >> 4) * 3 + pa) * 16);
+    }
+    f16x8 a[MFD_LPW][4];
+#pragma unroll
+    for (int L = 0; L < MFD_LPW; L++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            a[L][i] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                           ar, aoff, (uint32_t)((MFD_LPW * w + L) * 768 + i * 192), 0));
+    const MfdMat mg = mfd_mat(G, ps.e, row0, w), mu = mfd_mat(U, ps.e, row0, w);
+    mfd_mainloop<MFD_R, MFD_R / 2, G64>(
+        a, mg, mu, w, [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; },
+        [] {});
+    __syncthreads();
+    // rows row0 + 16 b + n of token t: gate partials in row block b, up in R/2 + b
+    for (int i = threadIdx.x; i < (MFD_R / 2) * QMOE_WAVE; i += blockDim.x) {
+        const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
+        const int t = l >> 4, f = row0 + 16 * b + (l & 15);
+        if (t >= ps.nt || f >= F) continue;
+        float gv = 0.f, uv = 0.f;
+        for (int k = 0; k < S; k++) {
+            gv += part_lds[(k * MFD_R + b) * QMOE_WAVE + l];
+            uv += part_lds[(k * MFD_R + MFD_R / 2 + b) * QMOE_WAVE + l];
+        }
+        const float inv = xs.f[tokp[ps.p0 + t]];
+        h[(int64_t)(ps.p0 + t) * F + f] = silu(gv * inv) * (uv * inv);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// down: block = one pass x 16 row blocks (256 output rows); the block splits
+// its pass's h rows into LDS, each wave takes its slice's operands into
+// registers, and the LDS is then reused for the partials.
+// out[tok] += w * y (f32 atomics).
+// ---------------------------------------------------------------------------
+template <bool G64>
+__global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
+    F32Mat D, const float *__restrict__ h, float *__restrict__ out,
+    const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp,
+    const float *__restrict__ wsort, int max_rec) {
+    // [NL][4][64] operands; first 16 bytes: row maxima; later the partials
+    extern __shared__ f16x8 lds_a[];
+    const int slot = blockIdx.z * gridDim.y + blockIdx.y;
+    if (slot >= max_rec) return;
+    const MfdPass ps = mfd_pass(rec, slot);
+    if (ps.e < 0 || ps.nt <= 0) return;
+    const int O = D.rows, K = D.cols, NL = K / SP_STEP;
+    const int row0 = blockIdx.x * (16 * MFD_R);
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const int lane = lane_id();
+    const int tid = threadIdx.x, nth = blockDim.x;
+    float inv[MFD_TB];
+    f16x8 a[MFD_LPW][4];
+    // split of the pass's h rows into LDS and this wave's operands into
+    // registers (runs while the first row blocks' weights are in flight);
+    // afterwards the LDS holds the partials
+    auto ready = [&] {
+        uint32_t *amax = reinterpret_cast<uint32_t *>(lds_a);
+        if (tid < MFD_TB) amax[tid] = 0u;
+        __syncthreads();
+        for (int t = 0; t < ps.nt; t++) {
+            const float *hr = h + (int64_t)(ps.p0 + t) * K;
+            // |x| as unsigned bits orders like |x| (NaN above inf)
+            uint32_t m = 0u;
+            for (int c = 4 * tid; c < K; c += 4 * nth) {
+                const f32x4 v = *(const f32x4 *)(hr + c);
+                m = max(m, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
+                               max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
+            }
+            if (m) atomicMax(&amax[t], m);
+        }
+        __syncthreads();
+        float sc[MFD_TB];
+#pragma unroll
+        for (int t = 0; t < MFD_TB; t++) sc[t] = sp_scale(__uint_as_float(amax[t]), &inv[t]);
+        __syncthreads();
+        const f16x8 z = {};
+        const int nvec = MFD_TB * NL * 16;
+        for (int v = tid; v < nvec; v += nth) {
+            const int t = v / (NL * 16), q = v - t * (NL * 16);
+            const int L = q >> 4, i = (q >> 2) & 3, gg = q & 3;
+            f16x8 *dst = lds_a + (L * 4 + i) * QMOE_WAVE + 16 * gg + 4 * t;
+            if (t < ps.nt) {
+                const float *src = h + (int64_t)(ps.p0 + t) * K + L * SP_STEP + sp_run(i, gg);
+                const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
+                const float run[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                f16x8 part[3];
+                sp_split8(run, sc[t], part);
+                dst[0] = part[0];
+                dst[1] = part[1];
+                dst[2] = part[2];
+            } else {
+                dst[0] = z;
+                dst[1] = z;
+                dst[2] = z;
+            }
+            dst[3] = z;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int L = 0; L < MFD_LPW; L++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                a[L][i] = lds_a[((MFD_LPW * w + L) * 4 + i) * QMOE_WAVE + lane];
+        __syncthreads();
+    };
+    float *part_lds = reinterpret_cast<float *>(lds_a);   // [S][R][64]
+    const MfdMat md = mfd_mat(D, ps.e, row0, w);
+    mfd_mainloop<MFD_R, MFD_R, G64>(
+        a, md, md, w,
+        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, ready);
+    __syncthreads();
+    const int S = K / MFD_KW;
+    for (int i = tid; i < MFD_R * QMOE_WAVE; i += nth) {
+        const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
+        const int t = l >> 4, o = row0 + 16 * b + (l & 15);
+        if (t >= ps.nt || o >= O) continue;
+        float y = 0.f;
+        for (int k = 0; k < S; k++) y += part_lds[(k * MFD_R + b) * QMOE_WAVE + l];
+        const int pos = ps.p0 + t;
+        const float iv = t == 0 ? inv[0] : t == 1 ? inv[1] : t == 2 ? inv[2] : inv[3];
+        unsafeAtomicAdd(out + (int64_t)tokp[pos] * O + o, wsort[pos] * iv * y);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+static bool mfd_group_ok(const QMat &m) { return m.group >= 64; }
+static bool mfd_g64(const QMat &m) { return m.group == 64 && m.cols > 64; }
+
+bool mfd_gateup_supported(const QMat &gate, const QMat &up) {
+    return gate.cols % MFD_KW == 0 && gate.cols <= MFD_KW * MFD_GU_WAVES &&
+           mfd_group_ok(gate) && mfd_group_ok(up);
+}
+
+bool mfd_down_supported(const QMat &down) {
+    return down.cols % MFD_KW == 0 && down.cols <= MFD_DOWN_MAX_COLS && mfd_group_ok(down);
+}
+
+static dim3 mfd_grid(unsigned x, int64_t slots) {
+    const int64_t gy = slots < 65535 ? (slots > 0 ? slots : 1) : 65535;
+    return dim3(x, (unsigned)gy, (unsigned)((slots + gy - 1) / gy));
+}
+
+hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
+                             const int32_t *rec, const int32_t *tok, int max_rec,
+                             hipStream_t st) {
+    if (!mfd_gateup_supported(gate, up)) return hipErrorInvalidValue;
+    const int64_t xs_bytes = xsplit_bytes(tokens, gate.cols);
+    if (xs_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int rows_per_block = 16 * MFD_R / 2;
+    const dim3 grid = mfd_grid((gate.rows + rows_per_block - 1) / rows_per_block, max_rec);
+    const dim3 block((gate.cols / MFD_KW) * QMOE_WAVE);
+    const size_t lds = (size_t)(gate.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
+    const F32Mat G = f32_mat(gate), U = f32_mat(up);
+    if (mfd_g64(gate) && mfd_g64(up))
+        hipLaunchKernelGGL((mfd_gateup_kernel<true>), grid, block, lds, st, G, U, xs, xs_bytes, h,
+                           rec, tok, max_rec);
+    else
+        hipLaunchKernelGGL((mfd_gateup_kernel<false>), grid, block, lds, st, G, U, xs, xs_bytes, h,
+                           rec, tok, max_rec);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfd_down(const QMat &down, const float *h, float *out, const int32_t *rec,
+                           const int32_t *tok, const float *wsort, int max_rec,
+                           hipStream_t st) {
+    if (!mfd_down_supported(down)) return hipErrorInvalidValue;
+    const int rows_per_block = 16 * MFD_R;
+    const dim3 grid = mfd_grid((down.rows + rows_per_block - 1) / rows_per_block, max_rec);
+    const dim3 block((down.cols / MFD_KW) * QMOE_WAVE);
+    // the split operands, or the partials (S x R x 64 floats), whichever is larger
+    const size_t split = (size_t)(down.cols / SP_STEP) * 4 * QMOE_WAVE * sizeof(f16x8);
+    const size_t parts = (size_t)(down.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
+    const size_t lds = split > parts ? split : parts;
+    const F32Mat D = f32_mat(down);
+    if (mfd_g64(down))
+        hipLaunchKernelGGL((mfd_down_kernel<true>), grid, block, lds, st, D, h, out, rec, tok, wsort,
+                           max_rec);
+    else
+        hipLaunchKernelGGL((mfd_down_kernel<false>), grid, block, lds, st, D, h, out, rec, tok,
+                           wsort, max_rec);
+    return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -86,11 +86,20 @@ struct DecodePlan {
     int tb_gu, tb_dn;
 };
 
+// Exact three-part f16 form of f32 activation rows (split16.h): v holds
+// [rows][cols / 128][4][4][3] operands of 8 f16, f[row] = 2^-E of the row.
+struct XSplit {
+    uint16_t *v;
+    float *f;
+};
+
 // Decode preparation in one launch: the worklist and plan (block 0), x ->
-// digits for all tokens, and out <- 0.
+// digits (xd.dig set) or x -> f16 parts (xs.v set) for all tokens, and
+// out <- 0.
 hipError_t launch_decode_prep(const int32_t *ids, const float *topk_w, int n, int k, int E,
                               const Worklist &wl, const DecodePlan &plan, const float *x,
-                              int tokens, int hidden, XDigits xd, float *out, hipStream_t st);
+                              int tokens, int hidden, XDigits xd, XSplit xs, float *out,
+                              hipStream_t st);
 
 // x -> digits only (matvec and the single-expert FFN): rows of `cols`
 // digits (a multiple of 32) from x rows of src_cols <= cols elements, the
@@ -168,6 +177,23 @@ hipError_t launch_f32_gateup(const QMat &gate, const QMat &up, const float *x, f
 // them); routed: out[tok] += w * y (atomics), else out[tok] = y.
 hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int h_cols,
                            float *out, const F32Route &r, int tb, bool routed, hipStream_t st);
+
+// Decode GEMVs on the matrix cores (f32 activations, record mode; the
+// arithmetic of the f32 GEMVs above).  xs: the exact f16 parts of x from the
+// preparation kernel; h rows are sorted positions; passes of at most MFD_TB
+// tokens (the plan's tb for these kernels).  The down kernel keeps its
+// pass's split h in LDS: at most MFD_DOWN_MAX_COLS inputs.
+constexpr int MFD_TB = 4;
+constexpr int MFD_DOWN_MAX_COLS = 2048;
+bool mfd_gateup_supported(const QMat &gate, const QMat &up);
+bool mfd_down_supported(const QMat &down);
+// Bytes of the split of `rows` activation rows of `cols` inputs.
+inline int64_t xsplit_bytes(int64_t rows, int64_t cols) { return rows * cols * 6; }
+hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
+                             const int32_t *rec, const int32_t *tok, int max_rec,
+                             hipStream_t st);
+hipError_t launch_mfd_down(const QMat &down, const float *h, float *out, const int32_t *rec,
+                           const int32_t *tok, const float *wsort, int max_rec, hipStream_t st);
 
 // Prefill (bf16 activations, MFMA).
 constexpr int MFMA_BM = 256;

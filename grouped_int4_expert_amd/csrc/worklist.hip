@@ -15,6 +15,7 @@
 // surplus blocks exit.
 #include "common.h"
 #include "launch.h"
+#include "split16.h"
 #include "wl_wave.h"
 
 namespace qmoe {
@@ -249,7 +250,7 @@ hipError_t launch_xdigits(const float *x, int rows, int cols, int src_cols, XDig
 __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ topk_w, int n, int k, int E,
     Worklist wl, DecodePlan plan, const float *__restrict__ x, int tokens, int hidden, XDigits xd,
-    float *__restrict__ out) {
+    XSplit xs, float *__restrict__ out) {
     if (blockIdx.x == 0) {
         __shared__ int cnt[WL_MAX_E + 1], run[WL_MAX_E + 1];
         if (wave_id() == 0) wl_wave(ids, topk_w, n, k, E, wl, plan, cnt, run);
@@ -259,6 +260,11 @@ __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
     const int64_t first = (int64_t)(blockIdx.x - 1) * hpb;
     const int64_t stride = (int64_t)(gridDim.x - 1) * hpb;
     if (xd.dig) xdigits_chunks(x, tokens, hidden, hidden, xd, first, stride);
+    if (xs.v) {
+        // one block per row: 16 inputs per thread cover rows up to 16384
+        __shared__ uint32_t red;
+        sp_split_rows<2>(x, tokens, hidden, xs.v, xs.f, blockIdx.x - 1, gridDim.x - 1, &red);
+    }
     const int64_t total = (int64_t)tokens * hidden;
     for (int64_t i = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < total;
          i += (int64_t)(gridDim.x - 1) * blockDim.x)
@@ -267,13 +273,14 @@ __global__ void __launch_bounds__(WL_THREADS) decode_prep_kernel(
 
 hipError_t launch_decode_prep(const int32_t *ids, const float *topk_w, int n, int k, int E,
                               const Worklist &wl, const DecodePlan &plan, const float *x,
-                              int tokens, int hidden, XDigits xd, float *out, hipStream_t st) {
+                              int tokens, int hidden, XDigits xd, XSplit xs, float *out,
+                              hipStream_t st) {
     const int64_t nchunks = (int64_t)tokens * (hidden / XD_CHUNK);
     int64_t g = (nchunks + 31) / 32;     // 32 half-waves per 1024-thread block
     if (g < 1) g = 1;
     if (g > 1024) g = 1024;
     hipLaunchKernelGGL(decode_prep_kernel, dim3((int)g + 1), dim3(WL_THREADS), 0, st, ids,
-                       topk_w, n, k, E, wl, plan, x, tokens, hidden, xd, out);
+                       topk_w, n, k, E, wl, plan, x, tokens, hidden, xd, xs, out);
     return hipGetLastError();
 }
 
