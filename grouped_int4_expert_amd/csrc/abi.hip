@@ -125,6 +125,7 @@ struct LayerWs {
     DecodePlan plan;
     float *hf;           // f32 path: h [pairs][F]
     XSplit xs;           // f32 path, matrix-core record mode: f16 parts of x
+    XSplit hs;           // ... and of h (the down projection's operands)
     uint16_t *x16, *h16;
     float *xinv;
     YBuf y;
@@ -157,9 +158,14 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
             L.plan.tok = c.take<int32_t>(n);
             L.plan.wsort = c.take<float>(n);
             L.plan.max_rec = (int)n;
-            if (H % 256 == 0 && xsplit_bytes(T, H) < ((int64_t)1 << 31)) {
+            if (H % 512 == 0 && xsplit_bytes(T, H) < ((int64_t)1 << 31)) {
                 L.xs.v = c.take<uint16_t>(xsplit_bytes(T, H) / 2);
                 L.xs.f = c.take<float>(T);
+                if (F % 512 == 0 && F <= MFD_DOWN_MAX_COLS &&
+                    xsplit_bytes(n, F) < ((int64_t)1 << 31)) {
+                    L.hs.v = c.take<uint16_t>(xsplit_bytes(n, F) / 2);
+                    L.hs.f = c.take<float>(n * (F / 64));
+                }
             }
         }
         L.hf = c.take<float>(n * F);
@@ -600,7 +606,7 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
     if (x_dtype == QMOE_F32) {
         // record mode runs the passes on the matrix cores where the shapes allow
         const bool mf_gu = n > F32_INLINE_MAX && L.xs.v && mfd_gateup_supported(G, U);
-        const bool mf_dn = n > F32_INLINE_MAX && mfd_down_supported(D);
+        const bool mf_dn = mf_gu && L.hs.v && mfd_down_supported(D);
         const int tb_gu = mf_gu ? MFD_TB : f32_tokens_per_pass((int)n, E, true);
         const int tb_dn = mf_dn ? MFD_TB : f32_tokens_per_pass((int)n, E, false);
         F32Route r{};
@@ -636,8 +642,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         }
         if (e == hipSuccess) {
             if (mf_gu)
-                e = launch_mfd_gateup(G, U, L.xs, tokens, L.hf, L.plan.rec_gu, L.plan.tok,
-                                      L.plan.max_rec, st);
+                e = launch_mfd_gateup(G, U, L.xs, tokens, L.hf, mf_dn ? L.hs : XSplit{},
+                                      L.plan.rec_gu, L.plan.tok, L.plan.max_rec, st);
             else
                 e = launch_f32_gateup(G, U, static_cast<const float *>(x), L.hf, r, tb_gu, st);
         }
@@ -646,8 +652,8 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         if (r.rec) r.rec = L.plan.rec_dn;
         if (e == hipSuccess) {
             if (mf_dn)
-                e = launch_mfd_down(D, L.hf, out, L.plan.rec_dn, L.plan.tok, L.plan.wsort,
-                                    L.plan.max_rec, st);
+                e = launch_mfd_down(D, L.hs, (int)n, out, L.plan.rec_dn, L.plan.tok,
+                                    L.plan.wsort, L.plan.max_rec, st);
             else
                 e = launch_f32_down(D, L.hf, F, F, out, r, tb_dn, true, st);
         }

@@ -91,11 +91,15 @@ __device__ __forceinline__ MfdMat mfd_mat(const F32Mat &M, int e, int row0, int 
 // steps; rows blocks b = 0..R-1 of matrix M0 (b < R0) or M1 (b >= R0, row
 // block b - R0); `part(b, y)` receives the lane's part sum of row block b.
 // Input k0 of the wave: MFD_KW * w.  G64: group 64 (scales of the slice are
-// 8 consecutive floats per row).  `ready()` runs once the first row blocks'
-// loads are issued, before `a` is read (it may fill `a`).
-template <int R, int R0, bool G64, typename Part, typename Ready>
+// 8 consecutive floats per row).  GF: gf holds per-lane factors of the
+// slice's 8 groups (the activation parts' power of two per 64 inputs), taken
+// into the group scales.  `ready()` runs once the first row blocks' loads
+// are issued, before `a` is read (it may fill `a`).
+template <int R, int R0, bool G64, bool GF, typename Part, typename Ready>
 __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const MfdMat &M0,
-                                             const MfdMat &M1, int w, Part part, Ready ready) {
+                                             const MfdMat &M1, int w,
+                                             const float (&gf)[2 * MFD_LPW], Part part,
+                                             Ready ready) {
     u32x4 wq[MFD_STAGES][MFD_LPW];
     float sc[MFD_STAGES][2 * MFD_LPW];
     // loads of row block b into stage st: the four load steps of each row
@@ -142,9 +146,10 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
             pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][1], b1, pa, 0, 0, 0);
             f32x4 pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][2], b2, zero, 0, 0, 0);
             pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][3], b3, pb, 0, 0, 0);
+            const float sa = GF ? sc[st][2 * L] * gf[2 * L] : sc[st][2 * L];
+            const float sb = GF ? sc[st][2 * L + 1] * gf[2 * L + 1] : sc[st][2 * L + 1];
 #pragma unroll
-            for (int v = 0; v < 4; v++)
-                tot[v] = fmaf(sc[st][2 * L], pa[v], fmaf(sc[st][2 * L + 1], pb[v], tot[v]));
+            for (int v = 0; v < 4; v++) tot[v] = fmaf(sa, pa[v], fmaf(sb, pb[v], tot[v]));
         }
         // parts of the lane's token (register 3 is the zero part), smallest first
         part(b, (tot[2] + tot[1]) + tot[0]);
@@ -161,13 +166,25 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
 
 // ---------------------------------------------------------------------------
 // gate+up: block = one pass x 8 row blocks (128 rows) of gate and of up;
-// h[p0 + t][f] = silu(g) * u.
+// h = silu(g) * u for rows row0 .. row0 + 127 of the pass's tokens, written
+// as f32 h[p0 + t][f] or (hs.v set) as the down projection's operands: the
+// three f16 parts of h scaled per 64 rows (two groups per block), hs.f the
+// group's 2^-E.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void sp_split1(float xs, _Float16 &a, _Float16 &b, _Float16 &c) {
+    a = (_Float16)xs;
+    const float r1 = xs - (float)a;
+    b = (_Float16)r1;
+    c = (_Float16)(r1 - (float)b);
+}
+
 template <bool G64>
 __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
-    F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h,
+    F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h, XSplit hs,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp, int max_rec) {
     extern __shared__ float part_lds[];   // [S][R][64]
+    __shared__ float hv[MFD_TB][16 * MFD_R / 2];
+    __shared__ uint32_t gmax[MFD_TB][2];
     const int slot = blockIdx.z * gridDim.y + blockIdx.y;
     if (slot >= max_rec) return;
     const MfdPass ps = mfd_pass(rec, slot);
@@ -194,14 +211,17 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
                 f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                            ar, aoff, (uint32_t)((MFD_LPW * w + L) * 768 + i * 192), 0));
     const MfdMat mg = mfd_mat(G, ps.e, row0, w), mu = mfd_mat(U, ps.e, row0, w);
-    mfd_mainloop<MFD_R, MFD_R / 2, G64>(
-        a, mg, mu, w, [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; },
-        [] {});
+    const float nogf[2 * MFD_LPW] = {};
+    mfd_mainloop<MFD_R, MFD_R / 2, G64, false>(
+        a, mg, mu, w, nogf,
+        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, [] {});
+    const int tid = threadIdx.x;
+    if (tid < 2 * MFD_TB) gmax[tid >> 1][tid & 1] = 0u;
     __syncthreads();
     // rows row0 + 16 b + n of token t: gate partials in row block b, up in R/2 + b
-    for (int i = threadIdx.x; i < (MFD_R / 2) * QMOE_WAVE; i += blockDim.x) {
+    for (int i = tid; i < (MFD_R / 2) * QMOE_WAVE; i += blockDim.x) {
         const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
-        const int t = l >> 4, f = row0 + 16 * b + (l & 15);
+        const int t = l >> 4, r = 16 * b + (l & 15), f = row0 + r;
         if (t >= ps.nt || f >= F) continue;
         float gv = 0.f, uv = 0.f;
         for (int k = 0; k < S; k++) {
@@ -209,94 +229,88 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
             uv += part_lds[(k * MFD_R + MFD_R / 2 + b) * QMOE_WAVE + l];
         }
         const float inv = xs.f[tokp[ps.p0 + t]];
-        h[(int64_t)(ps.p0 + t) * F + f] = silu(gv * inv) * (uv * inv);
+        const float hval = silu(gv * inv) * (uv * inv);
+        if (hs.v) {
+            hv[t][r] = hval;
+            // |h| as unsigned bits orders like |h| (NaN above inf)
+            atomicMax(&gmax[t][r >> 6], __float_as_uint(fabsf(hval)));
+        } else {
+            h[(int64_t)(ps.p0 + t) * F + f] = hval;
+        }
+    }
+    if (!hs.v) return;
+    __syncthreads();
+    // input r of the block's 128 (down's load step row0 / 128) sits in MFMA
+    // step i, lane group g, element e of the operand layout
+    const int NLd = F / SP_STEP;
+    for (int i = tid; i < ps.nt * 16 * MFD_R / 2; i += blockDim.x) {
+        const int t = i / (16 * MFD_R / 2), r = i % (16 * MFD_R / 2), f = row0 + r;
+        if (f >= F) continue;
+        float inv;
+        const float sc = sp_scale(__uint_as_float(gmax[t][r >> 6]), &inv);
+        _Float16 p[3];
+        sp_split1(hv[t][r] * sc, p[0], p[1], p[2]);
+        const int si = 2 * ((r >> 6) & 1) + ((r >> 3) & 1), g = ((r >> 5) & 1) + 2 * ((r >> 4) & 1);
+        const int e = 2 * (r & 3) + ((r >> 2) & 1);
+        const int64_t pos = ps.p0 + t;
+        _Float16 *dst = reinterpret_cast<_Float16 *>(hs.v) +
+                        ((((pos * NLd + row0 / SP_STEP) * 4 + si) * 4 + g) * 3) * 8 + e;
+        dst[0] = p[0];
+        dst[8] = p[1];
+        dst[16] = p[2];
+        if ((r & 63) == 0) hs.f[pos * (F / 64) + f / 64] = inv;
     }
 }
 
 // ---------------------------------------------------------------------------
-// down: block = one pass x 16 row blocks (256 output rows); the block splits
-// its pass's h rows into LDS, each wave takes its slice's operands into
-// registers, and the LDS is then reused for the partials.
-// out[tok] += w * y (f32 atomics).
+// down: block = one pass x 16 row blocks (256 output rows), operands from the
+// gate+up kernel's split of h (per 64 inputs a power of two, taken into the
+// group scales).  out[tok] += w * y (f32 atomics).
 // ---------------------------------------------------------------------------
 template <bool G64>
 __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
-    F32Mat D, const float *__restrict__ h, float *__restrict__ out,
+    F32Mat D, XSplit hs, int64_t hs_bytes, float *__restrict__ out,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp,
     const float *__restrict__ wsort, int max_rec) {
-    // [NL][4][64] operands; first 16 bytes: row maxima; later the partials
-    extern __shared__ f16x8 lds_a[];
+    extern __shared__ float part_lds[];   // [S][R][64]
     const int slot = blockIdx.z * gridDim.y + blockIdx.y;
     if (slot >= max_rec) return;
     const MfdPass ps = mfd_pass(rec, slot);
     if (ps.e < 0 || ps.nt <= 0) return;
-    const int O = D.rows, K = D.cols, NL = K / SP_STEP;
+    const int O = D.rows, K = D.cols, NL = K / SP_STEP, S = K / MFD_KW;
     const int row0 = blockIdx.x * (16 * MFD_R);
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
-    const int lane = lane_id();
-    const int tid = threadIdx.x, nth = blockDim.x;
-    float inv[MFD_TB];
+    const int lane = lane_id(), n = lane & 15, g = lane >> 4;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(hs.v, hs_bytes);
+    uint32_t aoff = OOB_OFFSET;
+    const int ta = n >> 2, pa = n & 3;
+    if (ta < ps.nt && pa < SP_PARTS)
+        aoff = (uint32_t)(((int64_t)(ps.p0 + ta) * NL * 48 + g * 3 + pa) * 16);
     f16x8 a[MFD_LPW][4];
-    // split of the pass's h rows into LDS and this wave's operands into
-    // registers (runs while the first row blocks' weights are in flight);
-    // afterwards the LDS holds the partials
-    auto ready = [&] {
-        uint32_t *amax = reinterpret_cast<uint32_t *>(lds_a);
-        if (tid < MFD_TB) amax[tid] = 0u;
-        __syncthreads();
-        for (int t = 0; t < ps.nt; t++) {
-            const float *hr = h + (int64_t)(ps.p0 + t) * K;
-            // |x| as unsigned bits orders like |x| (NaN above inf)
-            uint32_t m = 0u;
-            for (int c = 4 * tid; c < K; c += 4 * nth) {
-                const f32x4 v = *(const f32x4 *)(hr + c);
-                m = max(m, max(max(__float_as_uint(fabsf(v.x)), __float_as_uint(fabsf(v.y))),
-                               max(__float_as_uint(fabsf(v.z)), __float_as_uint(fabsf(v.w)))));
-            }
-            if (m) atomicMax(&amax[t], m);
-        }
-        __syncthreads();
-        float sc[MFD_TB];
 #pragma unroll
-        for (int t = 0; t < MFD_TB; t++) sc[t] = sp_scale(__uint_as_float(amax[t]), &inv[t]);
-        __syncthreads();
-        const f16x8 z = {};
-        const int nvec = MFD_TB * NL * 16;
-        for (int v = tid; v < nvec; v += nth) {
-            const int t = v / (NL * 16), q = v - t * (NL * 16);
-            const int L = q >> 4, i = (q >> 2) & 3, gg = q & 3;
-            f16x8 *dst = lds_a + (L * 4 + i) * QMOE_WAVE + 16 * gg + 4 * t;
-            if (t < ps.nt) {
-                const float *src = h + (int64_t)(ps.p0 + t) * K + L * SP_STEP + sp_run(i, gg);
-                const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 4);
-                const float run[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                f16x8 part[3];
-                sp_split8(run, sc[t], part);
-                dst[0] = part[0];
-                dst[1] = part[1];
-                dst[2] = part[2];
-            } else {
-                dst[0] = z;
-                dst[1] = z;
-                dst[2] = z;
-            }
-            dst[3] = z;
-        }
-        __syncthreads();
+    for (int L = 0; L < MFD_LPW; L++)
 #pragma unroll
-        for (int L = 0; L < MFD_LPW; L++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                a[L][i] = lds_a[((MFD_LPW * w + L) * 4 + i) * QMOE_WAVE + lane];
-        __syncthreads();
-    };
-    float *part_lds = reinterpret_cast<float *>(lds_a);   // [S][R][64]
+        for (int i = 0; i < 4; i++)
+            a[L][i] = __builtin_bit_cast(
+                f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                           ar, aoff, (uint32_t)((MFD_LPW * w + L) * 768 + i * 192), 0));
+    // group factors of the lane's token (D rows: token l / 16) for the
+    // slice's 8 groups
+    float gf[2 * MFD_LPW];
+    {
+        const int gt = g < ps.nt ? g : 0;
+        const f32x4 *fp =
+            reinterpret_cast<const f32x4 *>(hs.f + (int64_t)(ps.p0 + gt) * (K / 64) + 8 * w);
+        const f32x4 f0 = fp[0], f1 = fp[1];
+        gf[0] = f0.x; gf[1] = f0.y; gf[2] = f0.z; gf[3] = f0.w;
+        gf[4] = f1.x; gf[5] = f1.y; gf[6] = f1.z; gf[7] = f1.w;
+    }
     const MfdMat md = mfd_mat(D, ps.e, row0, w);
-    mfd_mainloop<MFD_R, MFD_R, G64>(
-        a, md, md, w,
-        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, ready);
+    mfd_mainloop<MFD_R, MFD_R, G64, true>(
+        a, md, md, w, gf,
+        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, [] {});
     __syncthreads();
-    const int S = K / MFD_KW;
+    const int tid = threadIdx.x, nth = blockDim.x;
     for (int i = tid; i < MFD_R * QMOE_WAVE; i += nth) {
         const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
         const int t = l >> 4, o = row0 + 16 * b + (l & 15);
@@ -304,8 +318,7 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
         float y = 0.f;
         for (int k = 0; k < S; k++) y += part_lds[(k * MFD_R + b) * QMOE_WAVE + l];
         const int pos = ps.p0 + t;
-        const float iv = t == 0 ? inv[0] : t == 1 ? inv[1] : t == 2 ? inv[2] : inv[3];
-        unsafeAtomicAdd(out + (int64_t)tokp[pos] * O + o, wsort[pos] * iv * y);
+        unsafeAtomicAdd(out + (int64_t)tokp[pos] * O + o, wsort[pos] * y);
     }
 }
 
@@ -330,9 +343,10 @@ static dim3 mfd_grid(unsigned x, int64_t slots) {
 }
 
 hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
-                             const int32_t *rec, const int32_t *tok, int max_rec,
+                             XSplit hs, const int32_t *rec, const int32_t *tok, int max_rec,
                              hipStream_t st) {
     if (!mfd_gateup_supported(gate, up)) return hipErrorInvalidValue;
+    if (hs.v && gate.rows % MFD_KW) return hipErrorInvalidValue;
     const int64_t xs_bytes = xsplit_bytes(tokens, gate.cols);
     if (xs_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int rows_per_block = 16 * MFD_R / 2;
@@ -342,31 +356,30 @@ hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int to
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
     if (mfd_g64(gate) && mfd_g64(up))
         hipLaunchKernelGGL((mfd_gateup_kernel<true>), grid, block, lds, st, G, U, xs, xs_bytes, h,
-                           rec, tok, max_rec);
+                           hs, rec, tok, max_rec);
     else
         hipLaunchKernelGGL((mfd_gateup_kernel<false>), grid, block, lds, st, G, U, xs, xs_bytes, h,
-                           rec, tok, max_rec);
+                           hs, rec, tok, max_rec);
     return hipGetLastError();
 }
 
-hipError_t launch_mfd_down(const QMat &down, const float *h, float *out, const int32_t *rec,
+hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, const int32_t *rec,
                            const int32_t *tok, const float *wsort, int max_rec,
                            hipStream_t st) {
     if (!mfd_down_supported(down)) return hipErrorInvalidValue;
+    const int64_t hs_bytes = xsplit_bytes(pairs, down.cols);
+    if (hs_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int rows_per_block = 16 * MFD_R;
     const dim3 grid = mfd_grid((down.rows + rows_per_block - 1) / rows_per_block, max_rec);
     const dim3 block((down.cols / MFD_KW) * QMOE_WAVE);
-    // the split operands, or the partials (S x R x 64 floats), whichever is larger
-    const size_t split = (size_t)(down.cols / SP_STEP) * 4 * QMOE_WAVE * sizeof(f16x8);
-    const size_t parts = (size_t)(down.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
-    const size_t lds = split > parts ? split : parts;
+    const size_t lds = (size_t)(down.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
     const F32Mat D = f32_mat(down);
     if (mfd_g64(down))
-        hipLaunchKernelGGL((mfd_down_kernel<true>), grid, block, lds, st, D, h, out, rec, tok, wsort,
-                           max_rec);
+        hipLaunchKernelGGL((mfd_down_kernel<true>), grid, block, lds, st, D, hs, hs_bytes, out, rec,
+                           tok, wsort, max_rec);
     else
-        hipLaunchKernelGGL((mfd_down_kernel<false>), grid, block, lds, st, D, h, out, rec, tok,
-                           wsort, max_rec);
+        hipLaunchKernelGGL((mfd_down_kernel<false>), grid, block, lds, st, D, hs, hs_bytes, out,
+                           rec, tok, wsort, max_rec);
     return hipGetLastError();
 }
 

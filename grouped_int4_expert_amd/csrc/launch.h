@@ -180,19 +180,21 @@ hipError_t launch_f32_down(const QMat &down, const float *hin, int64_t h_ld, int
 
 // Decode GEMVs on the matrix cores (f32 activations, record mode; the
 // arithmetic of the f32 GEMVs above).  xs: the exact f16 parts of x from the
-// preparation kernel; h rows are sorted positions; passes of at most MFD_TB
-// tokens (the plan's tb for these kernels).  The down kernel keeps its
-// pass's split h in LDS: at most MFD_DOWN_MAX_COLS inputs.
+// preparation kernel; passes of at most MFD_TB tokens (the plan's tb for
+// these kernels).  gate+up writes h as f32 rows (h, sorted positions) or,
+// for the matrix-core down projection, as that kernel's operands (hs: the
+// f16 parts of each 64 rows of h scaled by a power of two, hs.f[pos][F / 64]
+// its inverse).  The down projection needs a gate+up that wrote hs.
 constexpr int MFD_TB = 4;
-constexpr int MFD_DOWN_MAX_COLS = 2048;
+constexpr int MFD_DOWN_MAX_COLS = 6144;
 bool mfd_gateup_supported(const QMat &gate, const QMat &up);
 bool mfd_down_supported(const QMat &down);
 // Bytes of the split of `rows` activation rows of `cols` inputs.
 inline int64_t xsplit_bytes(int64_t rows, int64_t cols) { return rows * cols * 6; }
 hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
-                             const int32_t *rec, const int32_t *tok, int max_rec,
+                             XSplit hs, const int32_t *rec, const int32_t *tok, int max_rec,
                              hipStream_t st);
-hipError_t launch_mfd_down(const QMat &down, const float *h, float *out, const int32_t *rec,
+hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, const int32_t *rec,
                            const int32_t *tok, const float *wsort, int max_rec, hipStream_t st);
 
 // Prefill (bf16 activations, MFMA).
