@@ -99,6 +99,11 @@ def make_layer(qm, synth, seed, dev):
     return layer, codes, {k: w[k] for k in ("sg", "su", "sd")}
 
 
+# Sources of the decode gate+up kernels (the VALU and the matrix-core passes),
+# in the order their counter summary hashes them.
+DECODE_GU_SRC = ("gemv_f32.hip", "gemv_mfma.hip", "split16.h")
+
+
 def source_hash(paths):
     """sha256[:16] of the concatenated kernel sources."""
     import hashlib
@@ -875,14 +880,14 @@ def main():
     }
     dec_achieved = dec_gu_bytes / (dec_gu_ms * 1e-3)
     roof_decode = {
-        "kernel": (f"f32_gateup_kernel (decode gate+up, 128 experts, {CALLS} launches at each "
-                   f"of 1, 4 and 16 tokens)"),
+        "kernel": (f"decode gate+up (128 experts, {CALLS} launches at each of 1, 4 and 16 "
+                   f"tokens: f32_gateup_kernel at 1 and 4, mfd_gateup_kernel at 16)"),
         "bound": "hbm",
         "achieved": round(dec_achieved / 1e9, 1),
         "peak": round(HBM_PEAK / 1e9, 1),
         "unit": "GB/s",
         "frac": round(dec_achieved / HBM_PEAK, 4),
-        "traffic": load_traffic([os.path.join(csrc, "gemv_f32.hip")],
+        "traffic": load_traffic([os.path.join(csrc, f) for f in DECODE_GU_SRC],
                                 "f32_gateup_decode_e128_counters.md"),
         "alg_bytes_per_launch": dec_gu_bytes // dec_gu_launches,
         "avg_launch_ms": round(dec_gu_ms / dec_gu_launches, 5),
@@ -902,8 +907,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("f32 (decode: int4 codes unpacked to f32, f32 FMA, f32 group scale); "
-                  "bf16 x as f16 MFMA operands, f32 accumulate (prefill)"),
+        "dtype": ("f32 (decode: int4 codes unpacked to f32, f32 FMA, f32 group scale; at 16 "
+                  "tokens exact f16 parts of x and h with the codes on f16 MFMA, f32 accumulate, "
+                  "f32 group scale); bf16 x as f16 MFMA operands, f32 accumulate (prefill)"),
         "data": "synthetic",
         "config": {
             "workload": ("matvec_256x1024 + decode_e128_h4096_f1536_top8 (T=1,4,16; "

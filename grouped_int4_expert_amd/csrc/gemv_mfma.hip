@@ -22,25 +22,29 @@
 // 64-input group, steps 2 and 3 the second; each group's partial sums are
 // multiplied by the row's f32 scale and added to the f32 totals.
 //
+// Weight stream.  Each wave reads a row block's four load steps back to back
+// (256 contiguous bytes of each of 16 rows): a probe of this stream on
+// MI355X read 5.8 TB/s, against 4.2 TB/s when every row advanced only 64
+// bytes per step.
+//
 // gate+up reads the activation parts from the preparation kernel's split of
-// x (global memory, L2-resident); down splits its pass's h rows itself into
-// LDS, one split per block shared by its waves.  Records, rows of h and the
-// routed atomic adds into out are those of the record mode of the VALU
-// kernels.
+// x (L2-resident) and writes h as the down projection's parts (a power of
+// two per 64 rows of h, whose inverse goes into down's group scales); down
+// reads them the same way.  Records, sorted positions and the routed atomic
+// adds into out are those of the record mode of the VALU kernels.
 #include "common.h"
 #include "launch.h"
 #include "split16.h"
 
 namespace qmoe {
 
-// A block = one pass x MFD_R 16-row blocks x the whole input width: wave w
+// A block = one pass x RB 16-row blocks x the whole input width: wave w
 // takes inputs 512 w .. 512 w + 511 (four load steps), so its activation
 // operands (64 registers) are read once; it streams its R row blocks, each
 // as four back-to-back loads of 64 bytes per row (256 contiguous bytes), and
 // leaves one partial sum per row and token in LDS; the block adds the
-// slices' partials at the end.  gate+up: row blocks 0..R/2-1 of gate and the
+// slices' partials at the end.  gate+up: row blocks 0..RB/2-1 of gate and the
 // same rows of up.
-constexpr int MFD_R = 16;          // 16-row blocks per block
 constexpr int MFD_KW = 512;        // inputs per wave
 constexpr int MFD_LPW = MFD_KW / SP_STEP;
 constexpr int MFD_GU_WAVES = 12;   // gate+up inputs up to 6144
@@ -104,15 +108,16 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
     float sc[MFD_STAGES][2 * MFD_LPW];
     // loads of row block b into stage st: the four load steps of each row
     // back to back, then the slice's scales
+    // (a row block past R reads past the descriptors: no memory access)
     auto issue = [&](int b, int st) {
         __builtin_amdgcn_sched_barrier(0);
         const MfdMat &M = b < R0 ? M0 : M1;
         const int bb = b < R0 ? b : b - R0;
-        const uint32_t qo = M.qwave + (uint32_t)bb * M.q16;
+        const uint32_t qo = b < R ? M.qwave + (uint32_t)bb * M.q16 : OOB_OFFSET;
 #pragma unroll
         for (int L = 0; L < MFD_LPW; L++)
             wq[st][L] = __builtin_amdgcn_raw_buffer_load_b128(M.q, M.qlane, qo + 64u * L, 0);
-        const uint32_t so = M.swave + (uint32_t)bb * M.s16;
+        const uint32_t so = b < R ? M.swave + (uint32_t)bb * M.s16 : OOB_OFFSET;
         if constexpr (G64) {
             const uint32_t g0 = (uint32_t)(2 * MFD_LPW) * (uint32_t)w * 4u;
 #pragma unroll
@@ -154,13 +159,17 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
         // parts of the lane's token (register 3 is the zero part), smallest first
         part(b, (tot[2] + tot[1]) + tot[0]);
     };
+    static_assert(R % MFD_STAGES == 0, "row blocks per block");
 #pragma unroll
-    for (int b = 0; b < MFD_STAGES && b < R; b++) issue(b, b);
+    for (int st = 0; st < MFD_STAGES; st++) issue(st, st);
     ready();
+    for (int b = 0; b < R; b += MFD_STAGES) {
+        b = __builtin_amdgcn_readfirstlane(b);
 #pragma unroll
-    for (int b = 0; b < R; b++) {
-        compute(b, b % MFD_STAGES);
-        if (b + MFD_STAGES < R) issue(b + MFD_STAGES, b % MFD_STAGES);
+        for (int st = 0; st < MFD_STAGES; st++) {
+            compute(b + st, st);
+            issue(b + st + MFD_STAGES, st);
+        }
     }
 }
 
@@ -178,87 +187,108 @@ __device__ __forceinline__ void sp_split1(float xs, _Float16 &a, _Float16 &b, _F
     c = (_Float16)(r1 - (float)b);
 }
 
-template <bool G64>
+template <int RB, bool G64>
 __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
     F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h, XSplit hs,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp, int max_rec) {
-    extern __shared__ float part_lds[];   // [S][R][64]
-    __shared__ float hv[MFD_TB][16 * MFD_R / 2];
-    __shared__ uint32_t gmax[MFD_TB][2];
+    // [S][RB][64] partials; then h of the block [4][8 RB] and the group maxima [4][RB / 4]
+    extern __shared__ float part_lds[];
+    constexpr int ROWS = 16 * RB / 2;   // rows of gate (and of up) per block
     const int slot = blockIdx.z * gridDim.y + blockIdx.y;
     if (slot >= max_rec) return;
     const MfdPass ps = mfd_pass(rec, slot);
     if (ps.e < 0 || ps.nt <= 0) return;
     const int F = G.rows, NL = G.cols / SP_STEP, S = G.cols / MFD_KW;
-    const int row0 = blockIdx.x * (16 * MFD_R / 2);
+    const int row0 = blockIdx.x * ROWS;
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int lane = lane_id(), n = lane & 15;
-    // activation operands: A row m = n is token n / 4, part n % 4 (part 3 and
-    // missing tokens read past the descriptor: zero)
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(xs.v, xs_bytes);
-    uint32_t aoff = OOB_OFFSET;
-    const int ta = n >> 2, pa = n & 3;
-    if (ta < ps.nt && pa < SP_PARTS) {
-        const int tok = tokp[ps.p0 + ta];
-        aoff = (uint32_t)(((int64_t)tok * NL * 48 + (lane >> 4) * 3 + pa) * 16);
-    }
-    f16x8 a[MFD_LPW][4];
-#pragma unroll
-    for (int L = 0; L < MFD_LPW; L++)
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-            a[L][i] = __builtin_bit_cast(
-                f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                           ar, aoff, (uint32_t)((MFD_LPW * w + L) * 768 + i * 192), 0));
     const MfdMat mg = mfd_mat(G, ps.e, row0, w), mu = mfd_mat(U, ps.e, row0, w);
+    f16x8 a[MFD_LPW][4];
+    // activation operands (after the first weights are on their way): A row
+    // m = n is token n / 4, part n % 4 (part 3 and missing tokens read past
+    // the descriptor: zero)
+    auto ready = [&] {
+        const __amdgpu_buffer_rsrc_t ar = make_rsrc(xs.v, xs_bytes);
+        uint32_t aoff = OOB_OFFSET;
+        const int ta = n >> 2, pa = n & 3;
+        if (ta < ps.nt && pa < SP_PARTS) {
+            const int tok = tokp[ps.p0 + ta];
+            aoff = (uint32_t)(((int64_t)tok * NL * 48 + (lane >> 4) * 3 + pa) * 16);
+        }
+#pragma unroll
+        for (int L = 0; L < MFD_LPW; L++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                a[L][i] = __builtin_bit_cast(
+                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                               ar, aoff, (uint32_t)((MFD_LPW * w + L) * 768 + i * 192), 0));
+        // these are the newest loads: wait for them once here, not in every
+        // step of the row-block loop
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    };
     const float nogf[2 * MFD_LPW] = {};
-    mfd_mainloop<MFD_R, MFD_R / 2, G64, false>(
+    mfd_mainloop<RB, RB / 2, G64, false>(
         a, mg, mu, w, nogf,
-        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, [] {});
-    const int tid = threadIdx.x;
-    if (tid < 2 * MFD_TB) gmax[tid >> 1][tid & 1] = 0u;
+        [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, ready);
+    const int tid = threadIdx.x, nth = blockDim.x;
     __syncthreads();
-    // rows row0 + 16 b + n of token t: gate partials in row block b, up in R/2 + b
-    for (int i = tid; i < (MFD_R / 2) * QMOE_WAVE; i += blockDim.x) {
+    // rows row0 + 16 b + n of token t: gate partials in row block b, up in RB/2 + b
+    float hreg[RB / 2];
+#pragma unroll
+    for (int j = 0; j < RB / 2; j++) {
+        const int i = tid + j * nth;
+        hreg[j] = 0.f;
+        if (i >= (RB / 2) * QMOE_WAVE) continue;
         const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
-        const int t = l >> 4, r = 16 * b + (l & 15), f = row0 + r;
+        const int t = l >> 4, f = row0 + 16 * b + (l & 15);
         if (t >= ps.nt || f >= F) continue;
         float gv = 0.f, uv = 0.f;
         for (int k = 0; k < S; k++) {
-            gv += part_lds[(k * MFD_R + b) * QMOE_WAVE + l];
-            uv += part_lds[(k * MFD_R + MFD_R / 2 + b) * QMOE_WAVE + l];
+            gv += part_lds[(k * RB + b) * QMOE_WAVE + l];
+            uv += part_lds[(k * RB + RB / 2 + b) * QMOE_WAVE + l];
         }
         const float inv = xs.f[tokp[ps.p0 + t]];
-        const float hval = silu(gv * inv) * (uv * inv);
-        if (hs.v) {
-            hv[t][r] = hval;
-            // |h| as unsigned bits orders like |h| (NaN above inf)
-            atomicMax(&gmax[t][r >> 6], __float_as_uint(fabsf(hval)));
-        } else {
-            h[(int64_t)(ps.p0 + t) * F + f] = hval;
-        }
+        hreg[j] = silu(gv * inv) * (uv * inv);
+        if (!hs.v) h[(int64_t)(ps.p0 + t) * F + f] = hreg[j];
     }
     if (!hs.v) return;
+    float *hv = part_lds;                                        // [4][ROWS]
+    uint32_t *gmax = reinterpret_cast<uint32_t *>(part_lds + MFD_TB * ROWS);   // [4][ROWS / 64]
+    __syncthreads();   // every partial has been read
+    if (tid < MFD_TB * ROWS / 64) gmax[tid] = 0u;
     __syncthreads();
-    // input r of the block's 128 (down's load step row0 / 128) sits in MFMA
-    // step i, lane group g, element e of the operand layout
+#pragma unroll
+    for (int j = 0; j < RB / 2; j++) {
+        const int i = tid + j * nth;
+        if (i >= (RB / 2) * QMOE_WAVE) continue;
+        const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
+        const int t = l >> 4, r = 16 * b + (l & 15);
+        if (t >= ps.nt || row0 + r >= F) continue;
+        hv[t * ROWS + r] = hreg[j];
+        // |h| as unsigned bits orders like |h| (NaN above inf)
+        atomicMax(&gmax[t * (ROWS / 64) + (r >> 6)], __float_as_uint(fabsf(hreg[j])));
+    }
+    __syncthreads();
+    // input r of the block (down's load step (row0 + r) / 128, input r % 128
+    // of it) sits in MFMA step i, lane group g, element e of the operand layout
     const int NLd = F / SP_STEP;
-    for (int i = tid; i < ps.nt * 16 * MFD_R / 2; i += blockDim.x) {
-        const int t = i / (16 * MFD_R / 2), r = i % (16 * MFD_R / 2), f = row0 + r;
+    for (int i = tid; i < ps.nt * ROWS; i += nth) {
+        const int t = i / ROWS, r = i % ROWS, f = row0 + r;
         if (f >= F) continue;
         float inv;
-        const float sc = sp_scale(__uint_as_float(gmax[t][r >> 6]), &inv);
+        const float sc = sp_scale(__uint_as_float(gmax[t * (ROWS / 64) + (r >> 6)]), &inv);
         _Float16 p[3];
-        sp_split1(hv[t][r] * sc, p[0], p[1], p[2]);
-        const int si = 2 * ((r >> 6) & 1) + ((r >> 3) & 1), g = ((r >> 5) & 1) + 2 * ((r >> 4) & 1);
-        const int e = 2 * (r & 3) + ((r >> 2) & 1);
+        sp_split1(hv[t * ROWS + r] * sc, p[0], p[1], p[2]);
+        const int c = f % SP_STEP;
+        const int si = 2 * ((c >> 6) & 1) + ((c >> 3) & 1), g = ((c >> 5) & 1) + 2 * ((c >> 4) & 1);
+        const int e = 2 * (c & 3) + ((c >> 2) & 1);
         const int64_t pos = ps.p0 + t;
         _Float16 *dst = reinterpret_cast<_Float16 *>(hs.v) +
-                        ((((pos * NLd + row0 / SP_STEP) * 4 + si) * 4 + g) * 3) * 8 + e;
+                        ((((pos * NLd + f / SP_STEP) * 4 + si) * 4 + g) * 3) * 8 + e;
         dst[0] = p[0];
         dst[8] = p[1];
         dst[16] = p[2];
-        if ((r & 63) == 0) hs.f[pos * (F / 64) + f / 64] = inv;
+        if ((f & 63) == 0) hs.f[pos * (F / 64) + f / 64] = inv;
     }
 }
 
@@ -267,7 +297,7 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
 // gate+up kernel's split of h (per 64 inputs a power of two, taken into the
 // group scales).  out[tok] += w * y (f32 atomics).
 // ---------------------------------------------------------------------------
-template <bool G64>
+template <int RB, bool G64>
 __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
     F32Mat D, XSplit hs, int64_t hs_bytes, float *__restrict__ out,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp,
@@ -278,7 +308,7 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
     const MfdPass ps = mfd_pass(rec, slot);
     if (ps.e < 0 || ps.nt <= 0) return;
     const int O = D.rows, K = D.cols, NL = K / SP_STEP, S = K / MFD_KW;
-    const int row0 = blockIdx.x * (16 * MFD_R);
+    const int row0 = blockIdx.x * (16 * RB);
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const int lane = lane_id(), n = lane & 15, g = lane >> 4;
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(hs.v, hs_bytes);
@@ -306,17 +336,17 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
         gf[4] = f1.x; gf[5] = f1.y; gf[6] = f1.z; gf[7] = f1.w;
     }
     const MfdMat md = mfd_mat(D, ps.e, row0, w);
-    mfd_mainloop<MFD_R, MFD_R, G64, true>(
+    mfd_mainloop<RB, RB, G64, true>(
         a, md, md, w, gf,
-        [&](int b, float y) { part_lds[(w * MFD_R + b) * QMOE_WAVE + lane] = y; }, [] {});
+        [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, [] {});
     __syncthreads();
     const int tid = threadIdx.x, nth = blockDim.x;
-    for (int i = tid; i < MFD_R * QMOE_WAVE; i += nth) {
+    for (int i = tid; i < RB * QMOE_WAVE; i += nth) {
         const int b = i / QMOE_WAVE, l = i % QMOE_WAVE;
         const int t = l >> 4, o = row0 + 16 * b + (l & 15);
         if (t >= ps.nt || o >= O) continue;
         float y = 0.f;
-        for (int k = 0; k < S; k++) y += part_lds[(k * MFD_R + b) * QMOE_WAVE + l];
+        for (int k = 0; k < S; k++) y += part_lds[(k * RB + b) * QMOE_WAVE + l];
         const int pos = ps.p0 + t;
         unsafeAtomicAdd(out + (int64_t)tokp[pos] * O + o, wsort[pos] * y);
     }
@@ -342,6 +372,10 @@ static dim3 mfd_grid(unsigned x, int64_t slots) {
     return dim3(x, (unsigned)gy, (unsigned)((slots + gy - 1) / gy));
 }
 
+// 16-row blocks per block (32 measured no faster for gate+up and slower for
+// down, whose 16-token launch then has too few blocks to fill the GPU).
+static int mfd_rb(int) { return 16; }
+
 hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
                              XSplit hs, const int32_t *rec, const int32_t *tok, int max_rec,
                              hipStream_t st) {
@@ -349,18 +383,22 @@ hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int to
     if (hs.v && gate.rows % MFD_KW) return hipErrorInvalidValue;
     const int64_t xs_bytes = xsplit_bytes(tokens, gate.cols);
     if (xs_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const int rows_per_block = 16 * MFD_R / 2;
+    const int rb = mfd_rb(gate.cols);
+    const int rows_per_block = 16 * rb / 2;
     const dim3 grid = mfd_grid((gate.rows + rows_per_block - 1) / rows_per_block, max_rec);
     const dim3 block((gate.cols / MFD_KW) * QMOE_WAVE);
-    const size_t lds = (size_t)(gate.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
+    const size_t lds = (size_t)(gate.cols / MFD_KW) * rb * QMOE_WAVE * sizeof(float);
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
-    if (mfd_g64(gate) && mfd_g64(up))
-        hipLaunchKernelGGL((mfd_gateup_kernel<true>), grid, block, lds, st, G, U, xs, xs_bytes, h,
-                           hs, rec, tok, max_rec);
-    else
-        hipLaunchKernelGGL((mfd_gateup_kernel<false>), grid, block, lds, st, G, U, xs, xs_bytes, h,
-                           hs, rec, tok, max_rec);
-    return hipGetLastError();
+    const bool g64 = mfd_g64(gate) && mfd_g64(up);
+#define X(RB_, G_)                                                                              \
+    if (rb == RB_ && g64 == G_) {                                                               \
+        hipLaunchKernelGGL((mfd_gateup_kernel<RB_, G_>), grid, block, lds, st, G, U, xs,         \
+                           xs_bytes, h, hs, rec, tok, max_rec);                                 \
+        return hipGetLastError();                                                               \
+    }
+    X(16, true) X(16, false)
+#undef X
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, const int32_t *rec,
@@ -369,18 +407,22 @@ hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, c
     if (!mfd_down_supported(down)) return hipErrorInvalidValue;
     const int64_t hs_bytes = xsplit_bytes(pairs, down.cols);
     if (hs_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    const int rows_per_block = 16 * MFD_R;
+    const int rb = mfd_rb(down.cols);
+    const int rows_per_block = 16 * rb;
     const dim3 grid = mfd_grid((down.rows + rows_per_block - 1) / rows_per_block, max_rec);
     const dim3 block((down.cols / MFD_KW) * QMOE_WAVE);
-    const size_t lds = (size_t)(down.cols / MFD_KW) * MFD_R * QMOE_WAVE * sizeof(float);
+    const size_t lds = (size_t)(down.cols / MFD_KW) * rb * QMOE_WAVE * sizeof(float);
     const F32Mat D = f32_mat(down);
-    if (mfd_g64(down))
-        hipLaunchKernelGGL((mfd_down_kernel<true>), grid, block, lds, st, D, hs, hs_bytes, out, rec,
-                           tok, wsort, max_rec);
-    else
-        hipLaunchKernelGGL((mfd_down_kernel<false>), grid, block, lds, st, D, hs, hs_bytes, out,
-                           rec, tok, wsort, max_rec);
-    return hipGetLastError();
+    const bool g64 = mfd_g64(down);
+#define X(RB_, G_)                                                                              \
+    if (rb == RB_ && g64 == G_) {                                                               \
+        hipLaunchKernelGGL((mfd_down_kernel<RB_, G_>), grid, block, lds, st, D, hs, hs_bytes,    \
+                           out, rec, tok, wsort, max_rec);                                      \
+        return hipGetLastError();                                                               \
+    }
+    X(16, true) X(16, false)
+#undef X
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qmoe

@@ -26,7 +26,12 @@ BF16_TOL = 2e-3    # prefill path (bf16 activations, MFMA), relative L2
 #    rounding of u = 2^-24 per step of its longest chain: at most 32 FMAs per
 #    lane chunk, 1 scale product, 6 DPP adds, 7 slice and atomic adds, the
 #    SiLU (exp, add, divide, product: 4) -- C = 64 covers the depth of the
-#    gate+up chain plus the down chain with room.
+#    gate+up chain plus the down chain with room.  The matrix-core passes
+#    (planned calls) form the products exactly (x and h as three f16 parts,
+#    codes in f16) and round only in the additions: the MFMA's f32 sums of
+#    32 products (two per 64-input group), the group-scale FMAs (8 per
+#    512-input slice), the part and slice sums (at most 2 + 11) and the same
+#    SiLU and atomic steps, a chain no deeper than the VALU one.
 #  * bf16: q*s, h and every down product pass through one f16 rounding
 #    (u = 2^-11 relative) that M counts once each; the f16 Y blocks add at
 #    most one more, and the f32 accumulation is 2^13 times smaller: C = 2.

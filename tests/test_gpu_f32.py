@@ -189,3 +189,89 @@ def test_digit_variant_expert_ffn():
                              x.to(DEV), x_dtype=qm.QMOE_F32_DIGITS).cpu().numpy()
     ref = L.oracle_layer(x, torch.zeros(3, 1, dtype=torch.int32), torch.ones(3, 1))
     assert rel_l2(out, ref) <= F32_TOL
+
+
+# ---------------------------------------------------------------------------
+# Past 64 pairs, with input widths that are multiples of 512, the passes run
+# on the matrix cores: x and h carried as three exact f16 parts each, codes as
+# exact f16, products accumulated in f32, the f32 group scale per 64 inputs.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("H,F", [(1024, 512), (512, 1536), (1536, 1024), (1024, 320)])
+def test_matrix_core_layer_outlier_groups(H, F):
+    """Every 64-input group of x holds one element 1e4 times the others; the
+    widths give one, two, three and four waves per block (H or F = 512,
+    1024, 1536) and, at F = 320, a gate+up that writes f32 h for the VALU
+    down projection."""
+    E, T, k = 16, 24, 4
+    say(f"matrix-core layer E={E} H={H} F={F} T={T} k={k}, outlier groups")
+    L = Layer(E, H, F, seed=520)
+    g = synth.generator(521)
+    x = _outlier_x(g, T, H)
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, T, E), k)
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    err, _ = check(out, ref, mag, "f32", "layer")
+    assert err <= 1e-6
+
+
+def test_matrix_core_layer_nan_reaches_its_token_only():
+    say("matrix-core layer E=8 H=512 F=512 T=20 k=4, NaN in one token")
+    L = Layer(8, 512, 512, seed=522)
+    g = synth.generator(523)
+    x = synth.rand_x(g, (20, 512))
+    x[7, 300] = float("nan")
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, 20, 8), 4)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref = L.oracle_layer(x, ids, w)
+    assert np.isnan(ref[7]).all() and np.isnan(out[7]).all()
+    keep = [t for t in range(20) if t != 7]
+    assert np.isfinite(out[keep]).all()
+    check(out[keep], ref[keep], None, "f32", "other tokens")
+
+
+@pytest.mark.parametrize("counts_e", [16, 64, 1024])
+def test_matrix_core_layer_pass_grouping(counts_e):
+    """Experts with 1..17 pairs (passes of four tokens, the last one short;
+    duplicate experts in one token)."""
+    counts = [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 13, 16, 17]
+    T = sum(counts)
+    E = counts_e
+    say(f"matrix-core layer E={E} H=512 F=512 T={T} k=2, fixed pairs per expert")
+    L = Layer(E, 512, 512, seed=524)
+    perm = torch.randperm(2 * T, generator=torch.Generator().manual_seed(524))
+    assign = torch.repeat_interleave(torch.arange(len(counts)), torch.tensor(counts) * 2)[perm]
+    ids = (assign * (E // 16)).to(torch.int32).view(T, 2)
+    g = synth.generator(525)
+    x = synth.rand_x(g, (T, 512))
+    w = torch.rand((T, 2), generator=g)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
+
+
+@pytest.mark.parametrize("group", [128, 1024])
+def test_matrix_core_layer_wider_groups(group):
+    """Groups of 128 and one scale per row (1024 = the width of gate and up):
+    the general scale path of the matrix-core kernels."""
+    say(f"matrix-core layer E=16 H=1024 F=1024 T=24 k=4 group {group}")
+    L = Layer(16, 1024, 1024, seed=526, group=group)
+    g = synth.generator(527)
+    x = synth.rand_x(g, (24, 1024))
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, 24, 16), 4)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
+
+
+def test_matrix_core_layer_many_tokens_per_expert():
+    """129 tokens x top-8 over 16 experts: about 65 pairs per expert, 17
+    passes each, one short."""
+    say("matrix-core layer E=16 H=512 F=512 T=129 k=8")
+    L = Layer(16, 512, 512, seed=528)
+    g = synth.generator(529)
+    x = synth.rand_x(g, (129, 512))
+    ids, w = synth.route_topk_fast(synth.normal_logits(g, 129, 16), 8)
+    out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "f32", "layer")
