@@ -102,43 +102,46 @@ __device__ __forceinline__ MfdMat mfd_mat(const F32Mat &M, int e, int row0, int 
 template <int R, int R0, bool G64, bool GF, typename Part, typename Ready>
 __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const MfdMat &M0,
                                              const MfdMat &M1, int w,
-                                             const float (&gf)[2 * MFD_LPW], Part part,
-                                             Ready ready) {
+                                             const float (&gf)[2 * MFD_LPW], float *sl,
+                                             Part part, Ready ready) {
     u32x4 wq[MFD_STAGES][MFD_LPW];
-    float sc[MFD_STAGES][2 * MFD_LPW];
-    // loads of row block b into stage st: the four load steps of each row
-    // back to back, then the slice's scales
+    const int lane = lane_id(), g = lane >> 4, n = lane & 15;
+    // scales: lane (g, n) fetches the scales of row n for the slice's groups
+    // h = g and h = 4 + g straight into LDS (sl[st][h / 4][16 (h % 4) + n]),
+    // so in-flight scales hold no registers
+    uint32_t sv0[2], sv1[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+        const MfdMat &M = m ? M1 : M0;
+        sv0[m] = M.slane + ((uint32_t)(MFD_KW * w + 64 * g) >> M.gshift) * 4u;
+        sv1[m] = M.slane + ((uint32_t)(MFD_KW * w + 64 * (4 + g)) >> M.gshift) * 4u;
+    }
     // (a row block past R reads past the descriptors: no memory access)
     auto issue = [&](int b, int st) {
         __builtin_amdgcn_sched_barrier(0);
-        const MfdMat &M = b < R0 ? M0 : M1;
+        const int m = b < R0 ? 0 : 1;
+        const MfdMat &M = m ? M1 : M0;
         const int bb = b < R0 ? b : b - R0;
         const uint32_t qo = b < R ? M.qwave + (uint32_t)bb * M.q16 : OOB_OFFSET;
 #pragma unroll
         for (int L = 0; L < MFD_LPW; L++)
             wq[st][L] = __builtin_amdgcn_raw_buffer_load_b128(M.q, M.qlane, qo + 64u * L, 0);
         const uint32_t so = b < R ? M.swave + (uint32_t)bb * M.s16 : OOB_OFFSET;
-        if constexpr (G64) {
-            const uint32_t g0 = (uint32_t)(2 * MFD_LPW) * (uint32_t)w * 4u;
-#pragma unroll
-            for (int v = 0; v < 2 * MFD_LPW / 4; v++) {
-                const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(M.s, M.slane, so + g0 + 16u * v, 0);
-#pragma unroll
-                for (int c = 0; c < 4; c++) sc[st][4 * v + c] = __uint_as_float(t[c]);
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2 * MFD_LPW; h++) {
-                const uint32_t gi = ((uint32_t)(MFD_KW * w + 64 * h) >> M.gshift) * 4u;
-                sc[st][h] = __uint_as_float(
-                    __builtin_amdgcn_raw_buffer_load_b32(M.s, M.slane, so + gi, 0));
-            }
-        }
+        float *dst = sl + st * 2 * QMOE_WAVE;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(M.s, QMOE_LDS(dst), 4, m ? sv0[1] : sv0[0], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(M.s, QMOE_LDS(dst + QMOE_WAVE), 4,
+                                                 m ? sv1[1] : sv1[0], so, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
+    // loads per stage, in issue order: MFD_LPW weight loads, 2 scale loads
+    constexpr int LPS = MFD_LPW + 2;
     auto compute = [&](int b, int st) {
+        // the scales of stage st arrive in LDS, which the compiler does not
+        // track: wait until only the later stages' loads are in flight
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS * (MFD_STAGES - 1)));
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         f32x4 tot = zero;
+        const float *ss = sl + st * 2 * QMOE_WAVE + n;
 #pragma unroll
         for (int L = 0; L < MFD_LPW; L++) {
             const u32x4 q = wq[st][L];
@@ -151,8 +154,11 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
             pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][1], b1, pa, 0, 0, 0);
             f32x4 pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][2], b2, zero, 0, 0, 0);
             pb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[L][3], b3, pb, 0, 0, 0);
-            const float sa = GF ? sc[st][2 * L] * gf[2 * L] : sc[st][2 * L];
-            const float sb = GF ? sc[st][2 * L + 1] * gf[2 * L + 1] : sc[st][2 * L + 1];
+            const int h0 = 2 * L, h1 = 2 * L + 1;
+            const float s0 = ss[(h0 / 4) * QMOE_WAVE + 16 * (h0 % 4)];
+            const float s1 = ss[(h1 / 4) * QMOE_WAVE + 16 * (h1 % 4)];
+            const float sa = GF ? s0 * gf[h0] : s0;
+            const float sb = GF ? s1 * gf[h1] : s1;
 #pragma unroll
             for (int v = 0; v < 4; v++) tot[v] = fmaf(sa, pa[v], fmaf(sb, pb[v], tot[v]));
         }
@@ -227,8 +233,9 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     };
     const float nogf[2 * MFD_LPW] = {};
+    float *sl = part_lds + S * RB * QMOE_WAVE + w * MFD_STAGES * 2 * QMOE_WAVE;
     mfd_mainloop<RB, RB / 2, G64, false>(
-        a, mg, mu, w, nogf,
+        a, mg, mu, w, nogf, sl,
         [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, ready);
     const int tid = threadIdx.x, nth = blockDim.x;
     __syncthreads();
@@ -336,8 +343,9 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
         gf[4] = f1.x; gf[5] = f1.y; gf[6] = f1.z; gf[7] = f1.w;
     }
     const MfdMat md = mfd_mat(D, ps.e, row0, w);
+    float *sl = part_lds + S * RB * QMOE_WAVE + w * MFD_STAGES * 2 * QMOE_WAVE;
     mfd_mainloop<RB, RB, G64, true>(
-        a, md, md, w, gf,
+        a, md, md, w, gf, sl,
         [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, [] {});
     __syncthreads();
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -376,6 +384,13 @@ static dim3 mfd_grid(unsigned x, int64_t slots) {
 // down, whose 16-token launch then has too few blocks to fill the GPU).
 static int mfd_rb(int) { return 16; }
 
+// LDS of a block: the partials [S][RB][64] and each wave's scale stages
+// [MFD_STAGES][2][64], floats.
+static size_t mfd_lds(int cols, int rb) {
+    const int S = cols / MFD_KW;
+    return (size_t)S * (rb + MFD_STAGES * 2) * QMOE_WAVE * sizeof(float);
+}
+
 hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int tokens, float *h,
                              XSplit hs, const int32_t *rec, const int32_t *tok, int max_rec,
                              hipStream_t st) {
@@ -387,7 +402,7 @@ hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int to
     const int rows_per_block = 16 * rb / 2;
     const dim3 grid = mfd_grid((gate.rows + rows_per_block - 1) / rows_per_block, max_rec);
     const dim3 block((gate.cols / MFD_KW) * QMOE_WAVE);
-    const size_t lds = (size_t)(gate.cols / MFD_KW) * rb * QMOE_WAVE * sizeof(float);
+    const size_t lds = mfd_lds(gate.cols, rb);
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
     const bool g64 = mfd_g64(gate) && mfd_g64(up);
 #define X(RB_, G_)                                                                              \
@@ -411,7 +426,7 @@ hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, c
     const int rows_per_block = 16 * rb;
     const dim3 grid = mfd_grid((down.rows + rows_per_block - 1) / rows_per_block, max_rec);
     const dim3 block((down.cols / MFD_KW) * QMOE_WAVE);
-    const size_t lds = (size_t)(down.cols / MFD_KW) * rb * QMOE_WAVE * sizeof(float);
+    const size_t lds = mfd_lds(down.cols, rb);
     const F32Mat D = f32_mat(down);
     const bool g64 = mfd_g64(down);
 #define X(RB_, G_)                                                                              \
