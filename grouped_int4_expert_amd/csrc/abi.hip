@@ -158,17 +158,24 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
             L.plan.tok = c.take<int32_t>(n);
             L.plan.wsort = c.take<float>(n);
             L.plan.max_rec = (int)n;
-            if (H % 512 == 0 && xsplit_bytes(T, H) < ((int64_t)1 << 31)) {
-                L.xs.v = c.take<uint16_t>(xsplit_bytes(T, H) / 2);
-                L.xs.f = c.take<float>(T);
-                if (F % 512 == 0 && F <= MFD_DOWN_MAX_COLS &&
-                    xsplit_bytes(n, F) < ((int64_t)1 << 31)) {
-                    L.hs.v = c.take<uint16_t>(xsplit_bytes(n, F) / 2);
-                    L.hs.f = c.take<float>(n * (F / 64));
-                }
-            }
         }
-        L.hf = c.take<float>(n * F);
+        bool hs_ok = false;
+        if (n > F32_INLINE_MAX && H % 512 == 0 && xsplit_bytes(T, H) < ((int64_t)1 << 31)) {
+            L.xs.v = c.take<uint16_t>(xsplit_bytes(T, H) / 2);
+            L.xs.f = c.take<float>(T);
+            hs_ok = F % 512 == 0 && F <= MFD_DOWN_MAX_COLS && xsplit_bytes(n, F) < ((int64_t)1 << 31);
+        }
+        if (hs_ok) {
+            // h is either f32 rows (VALU down) or the matrix-core down
+            // projection's f16 parts, never both in one call: one region
+            const int64_t hb = xsplit_bytes(n, F) > n * F * 4 ? xsplit_bytes(n, F) : n * F * 4;
+            uint16_t *hr = c.take<uint16_t>(hb / 2);
+            L.hf = reinterpret_cast<float *>(hr);
+            L.hs.v = hr;
+            L.hs.f = c.take<float>(n * (F / 64));
+        } else {
+            L.hf = c.take<float>(n * F);
+        }
     } else if (dtype == QMOE_F32_DIGITS) {
         L.plan.rec_gu = c.take<int32_t>(4 * n);
         L.plan.rec_dn = c.take<int32_t>(4 * n);

@@ -80,7 +80,15 @@ enum {
  *    accumulated in f32 per 64-input group, the group's f32 scale applied
  *    once per group (the grouped kernel of the colibri pull request, comment
  *    "blocked by GPU driver instability"); h = silu(g) * u is kept in f32.
- *    Widths: hidden <= 8192 into gate/up, inter <= 16384 into down.
+ *    Widths: hidden <= 8192 into gate/up, inter <= 16384 into down.  In
+ *    qmoe_layer calls of more than 64 pairs with groups of 64 or more and
+ *    widths that are multiples of 512 (hidden <= 6144 for gate/up, inter
+ *    <= 6144 for down) the weight passes run on the matrix cores with the
+ *    same arithmetic: each activation row (x, and each 64 inputs of h) is
+ *    scaled by a power of two and split into three f16 parts that sum to it
+ *    exactly (elements more than 2^15 below the largest keep an error below
+ *    2^-39 of it), the codes are exact in f16, so every product is exact,
+ *    and the sums are f32.
  *  - QMOE_F32_DIGITS: x is also f32 [tokens][H], but the activations are
  *    rounded to 18-bit block fixed point (one power-of-two exponent per
  *    64-element group of x and per 32-element chunk of h) and multiplied
@@ -337,8 +345,10 @@ size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
  * once per call and the later passes read them from the L2 cache.  With
  * QMOE_F32 and at most 64 pairs (tokens * k) the call is two kernel launches
  * (gate+up, which also groups the pairs by expert, then down); beyond that a
- * preparation kernel plans the passes once (three launches: faster from 128
- * pairs on, where every gate+up block would otherwise scan all the ids).
+ * preparation kernel plans the passes once and splits x into its f16 parts
+ * (three launches: faster from 128 pairs on, where every gate+up block would
+ * otherwise scan all the ids), and the passes, of up to four tokens, run on
+ * the matrix cores where the shapes allow (see QMOE_F32).
  * Reproducibility: the bf16 path sums each token's k expert rows in pick
  * order and gives bit-identical results from run to run; the f32 paths add
  * the k expert terms into out with f32 atomics, so their order, and the
@@ -396,7 +406,7 @@ int qmoe_layer_ws_layout(const qmoe_layer_desc *desc, int32_t tokens,
  * Nothing is allocated or freed and nothing in the array needs to start at
  * zero.  A call whose qmoe_layer_workspace_bytes exceeds the array returns
  * QMOE_ERR_SCRATCH and launches nothing (at hidden 4096, intermediate 1536
- * and top-8, the 64 MiB hold the f32 path up to 1,354 tokens, the digits
+ * and top-8, the 64 MiB hold the f32 path up to 674 tokens, the digits
  * variant up to 1,546 and the bf16 path up to 668 tokens).  Every call on one
  * GPU shares that GPU's array: calls that overlap in time on one
  * GPU (different streams, or different host threads without ordering) race
