@@ -186,13 +186,6 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
 // three f16 parts of h scaled per 64 rows (two groups per block), hs.f the
 // group's 2^-E.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void sp_split1(float xs, _Float16 &a, _Float16 &b, _Float16 &c) {
-    a = (_Float16)xs;
-    const float r1 = xs - (float)a;
-    b = (_Float16)r1;
-    c = (_Float16)(r1 - (float)b);
-}
-
 template <int RB, bool G64>
 __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
     F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h, XSplit hs,

@@ -55,18 +55,24 @@ __device__ __forceinline__ float sp_scale(float amax, float *inv) {
     return __uint_as_float((uint32_t)(127 + e) << 23);
 }
 
+// The three parts of one scaled element.  An infinity or NaN stays in the
+// first part (the residual inf - inf would turn an infinity into NaN).
+__device__ __forceinline__ void sp_split1(float xs, _Float16 &a, _Float16 &b, _Float16 &c) {
+    a = (_Float16)xs;
+    const float r1 = __builtin_isfinite(xs) ? xs - (float)a : 0.f;
+    b = (_Float16)r1;
+    c = (_Float16)(r1 - (float)b);
+}
+
 // The three parts of 8 scaled elements of one run, in element order.
 __device__ __forceinline__ void sp_split8(const float (&run)[8], float scale, f16x8 (&part)[3]) {
 #pragma unroll
     for (int e = 0; e < 8; e++) {
-        const float xs = run[sp_elem(e)] * scale;
-        const _Float16 a = (_Float16)xs;
-        const float r1 = xs - (float)a;
-        const _Float16 b = (_Float16)r1;
-        const float r2 = r1 - (float)b;
+        _Float16 a, b, c;
+        sp_split1(run[sp_elem(e)] * scale, a, b, c);
         part[0][e] = a;
         part[1][e] = b;
-        part[2][e] = (_Float16)r2;
+        part[2][e] = c;
     }
 }
 
