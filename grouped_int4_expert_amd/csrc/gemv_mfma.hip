@@ -92,14 +92,13 @@ __device__ __forceinline__ MfdMat mfd_mat(const F32Mat &M, int e, int row0, int 
 }
 
 // Main loop of one wave: a[L][i] = activation operands of its four load
-// steps; rows blocks b = 0..R-1 of matrix M0 (b < R0) or M1 (b >= R0, row
+// steps; row blocks b = 0..R-1 of matrix M0 (b < R0) or M1 (b >= R0, row
 // block b - R0); `part(b, y)` receives the lane's part sum of row block b.
-// Input k0 of the wave: MFD_KW * w.  G64: group 64 (scales of the slice are
-// 8 consecutive floats per row).  GF: gf holds per-lane factors of the
+// Input k0 of the wave: MFD_KW * w.  GF: gf holds per-lane factors of the
 // slice's 8 groups (the activation parts' power of two per 64 inputs), taken
 // into the group scales.  `ready()` runs once the first row blocks' loads
 // are issued, before `a` is read (it may fill `a`).
-template <int R, int R0, bool G64, bool GF, typename Part, typename Ready>
+template <int R, int R0, bool GF, typename Part, typename Ready>
 __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const MfdMat &M0,
                                              const MfdMat &M1, int w,
                                              const float (&gf)[2 * MFD_LPW], float *sl,
@@ -186,7 +185,7 @@ __device__ __forceinline__ void mfd_mainloop(const f16x8 (&a)[MFD_LPW][4], const
 // three f16 parts of h scaled per 64 rows (two groups per block), hs.f the
 // group's 2^-E.
 // ---------------------------------------------------------------------------
-template <int RB, bool G64>
+template <int RB>
 __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
     F32Mat G, F32Mat U, XSplit xs, int64_t xs_bytes, float *__restrict__ h, XSplit hs,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp, int max_rec) {
@@ -227,7 +226,7 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
     };
     const float nogf[2 * MFD_LPW] = {};
     float *sl = part_lds + S * RB * QMOE_WAVE + w * MFD_STAGES * 2 * QMOE_WAVE;
-    mfd_mainloop<RB, RB / 2, G64, false>(
+    mfd_mainloop<RB, RB / 2, false>(
         a, mg, mu, w, nogf, sl,
         [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, ready);
     const int tid = threadIdx.x, nth = blockDim.x;
@@ -297,7 +296,7 @@ __global__ void __launch_bounds__(MFD_GU_WAVES * QMOE_WAVE) mfd_gateup_kernel(
 // gate+up kernel's split of h (per 64 inputs a power of two, taken into the
 // group scales).  out[tok] += w * y (f32 atomics).
 // ---------------------------------------------------------------------------
-template <int RB, bool G64>
+template <int RB>
 __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
     F32Mat D, XSplit hs, int64_t hs_bytes, float *__restrict__ out,
     const int32_t *__restrict__ rec, const int32_t *__restrict__ tokp,
@@ -337,7 +336,7 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
     }
     const MfdMat md = mfd_mat(D, ps.e, row0, w);
     float *sl = part_lds + S * RB * QMOE_WAVE + w * MFD_STAGES * 2 * QMOE_WAVE;
-    mfd_mainloop<RB, RB, G64, true>(
+    mfd_mainloop<RB, RB, true>(
         a, md, md, w, gf, sl,
         [&](int b, float y) { part_lds[(w * RB + b) * QMOE_WAVE + lane] = y; }, [] {});
     __syncthreads();
@@ -357,7 +356,6 @@ __global__ void __launch_bounds__(MFD_DN_WAVES * QMOE_WAVE) mfd_down_kernel(
 // Host side
 // ---------------------------------------------------------------------------
 static bool mfd_group_ok(const QMat &m) { return m.group >= 64; }
-static bool mfd_g64(const QMat &m) { return m.group == 64 && m.cols > 64; }
 
 bool mfd_gateup_supported(const QMat &gate, const QMat &up) {
     return gate.cols % MFD_KW == 0 && gate.cols <= MFD_KW * MFD_GU_WAVES &&
@@ -397,14 +395,13 @@ hipError_t launch_mfd_gateup(const QMat &gate, const QMat &up, XSplit xs, int to
     const dim3 block((gate.cols / MFD_KW) * QMOE_WAVE);
     const size_t lds = mfd_lds(gate.cols, rb);
     const F32Mat G = f32_mat(gate), U = f32_mat(up);
-    const bool g64 = mfd_g64(gate) && mfd_g64(up);
-#define X(RB_, G_)                                                                              \
-    if (rb == RB_ && g64 == G_) {                                                               \
-        hipLaunchKernelGGL((mfd_gateup_kernel<RB_, G_>), grid, block, lds, st, G, U, xs,         \
-                           xs_bytes, h, hs, rec, tok, max_rec);                                 \
+#define X(RB_)                                                                                  \
+    if (rb == RB_) {                                                                            \
+        hipLaunchKernelGGL((mfd_gateup_kernel<RB_>), grid, block, lds, st, G, U, xs, xs_bytes,   \
+                           h, hs, rec, tok, max_rec);                                           \
         return hipGetLastError();                                                               \
     }
-    X(16, true) X(16, false)
+    X(16)
 #undef X
     return hipErrorInvalidValue;
 }
@@ -421,14 +418,13 @@ hipError_t launch_mfd_down(const QMat &down, XSplit hs, int pairs, float *out, c
     const dim3 block((down.cols / MFD_KW) * QMOE_WAVE);
     const size_t lds = mfd_lds(down.cols, rb);
     const F32Mat D = f32_mat(down);
-    const bool g64 = mfd_g64(down);
-#define X(RB_, G_)                                                                              \
-    if (rb == RB_ && g64 == G_) {                                                               \
-        hipLaunchKernelGGL((mfd_down_kernel<RB_, G_>), grid, block, lds, st, D, hs, hs_bytes,    \
-                           out, rec, tok, wsort, max_rec);                                      \
+#define X(RB_)                                                                                  \
+    if (rb == RB_) {                                                                            \
+        hipLaunchKernelGGL((mfd_down_kernel<RB_>), grid, block, lds, st, D, hs, hs_bytes, out,   \
+                           rec, tok, wsort, max_rec);                                           \
         return hipGetLastError();                                                               \
     }
-    X(16, true) X(16, false)
+    X(16)
 #undef X
     return hipErrorInvalidValue;
 }
