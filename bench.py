@@ -101,7 +101,7 @@ def make_layer(qm, synth, seed, dev):
 
 # Sources of the decode gate+up kernels (the VALU and the matrix-core passes),
 # in the order their counter summary hashes them.
-DECODE_GU_SRC = ("gemv_f32.hip", "gemv_mfma.hip", "split16.h")
+DECODE_GU_SRC = ("gemv_f32.hip", "gemv_mfma.hip", "mfd_loop.h", "split16.h")
 
 
 def source_hash(paths):
@@ -447,7 +447,7 @@ def time_layer_e256(qm, synth, torch, dev, calls=16, reps=3):
         "TFLOPs": round(pf / (best * 1e-3) / 1e12, 1),
         "frac_of_roofline": round(proof / (best * 1e-3), 4),
         "bound": "hbm" if pb / HBM_PEAK > pf / BF16_PEAK else "mfma",
-        "alg_bytes": pb, "alg_flops": pf,
+        "alg_bytes": pb, "alg_flops": pf, "pass_rows": qm.qmoe_prefill_pass_rows(),
         "phase_ms": {"worklist": round(ph[0], 4), "gate_up": round(ph[1], 4),
                      "down": round(ph[2], 4), "combine": round(ph[3], 4)}}
     res["config"] = {"workload": "layer_e256_h6144_f2048_top8_zipf1.1", "experts": E2,

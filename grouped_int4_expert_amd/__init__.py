@@ -64,7 +64,7 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
            "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_cache_device_state_bytes",
            "qmoe_cache_device_init", "qmoe_cache_prepare_device", "qmoe_layer_logits_workspace_bytes",
-           "qmoe_layer_logits", "qmoe_layer_noalloc"]
+           "qmoe_layer_logits", "qmoe_layer_noalloc", "qmoe_prefill_pass_rows"]
 
 _lib = None
 
@@ -119,6 +119,7 @@ def load(path: str | None = None):
                                              vp, vp, sz, vp]),
         "qmoe_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp,
                                               vp, i32, vp, vp]),
+        "qmoe_prefill_pass_rows": (i32, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -170,6 +171,11 @@ def _dev(t, name, dtype=None):
 
 def qmoe_abi_version() -> int:
     return int(load().qmoe_abi_version())
+
+
+def qmoe_prefill_pass_rows() -> int:
+    """Experts with at most this many pairs take the bf16 prefill passes."""
+    return int(load().qmoe_prefill_pass_rows())
 
 
 def qmoe_status_str(status: int) -> str:

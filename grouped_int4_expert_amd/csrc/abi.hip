@@ -1,7 +1,10 @@
 // C ABI of libqmoe.so: host-side validation, workspace layout and launch
 // sequencing.  Every check runs before the first HIP call, so a rejected
 // call launches nothing (fail closed).
+#include <stdlib.h>
 #include <string.h>
+
+#include <algorithm>
 
 #include "../../include/qmoe.h"
 #include "launch.h"
@@ -131,8 +134,22 @@ struct LayerWs {
     YBuf y;
     int64_t bytes;
     int max_active, max_tiles;
+    int max_passes;      // bf16 prefill passes (0: every expert takes tiles)
     qmoe_layer_ws_view view;
 };
+
+// Experts with at most this many pairs run the bf16 prefill as 16-row passes
+// (skinny.hip) rather than row tiles; QMOE_PREFILL_PASS_ROWS overrides it
+// (0 turns the passes off), read once per process.
+static int prefill_pass_rows() {
+    static const int v = [] {
+        const char *s = getenv("QMOE_PREFILL_PASS_ROWS");
+        int r = PREFILL_PASS_ROWS_DEFAULT;
+        if (s && *s) r = atoi(s);
+        return r < 0 ? 0 : (r > MFMA_BM ? MFMA_BM : r);
+    }();
+    return v;
+}
 
 LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
     LayerWs L{};
@@ -192,6 +209,15 @@ LayerWs carve_layer(void *ws, int E, int H, int F, int T, int k, int dtype) {
         L.h16 = c.take<uint16_t>(n * F);
         L.y.v = c.take<uint16_t>(n * H);
         L.y.e = c.take<int8_t>(n * (H / 16));
+        const int pm = prefill_pass_rows();
+        if (pm > 0) {
+            const int64_t per_expert = (pm + SK_TP - 1) / SK_TP;
+            const int64_t bound = (n + SK_TP - 1) / SK_TP + L.max_active;
+            L.max_passes = (int)std::min(bound, per_expert * L.max_active);
+            L.wl.spass = c.take<int32_t>(2 * (int64_t)L.max_passes);
+            L.wl.n_spass = c.take<int32_t>(1);
+            L.wl.skinny_max = pm;
+        }
     }
     L.bytes = c.off;
     // offsets of the worklist arrays (same order as above)
@@ -521,6 +547,8 @@ int qmoe_worklist(const int32_t *topk_ids, int32_t tokens, int32_t k, int32_t ex
                                      static_cast<int32_t *>(ws), as_stream(stream)));
 }
 
+int32_t qmoe_prefill_pass_rows(void) { return prefill_pass_rows(); }
+
 size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens, int32_t k,
                                   int32_t x_dtype) {
     if (!desc || tokens < 0 || k < 1 || desc->experts < 1) return 0;
@@ -689,7 +717,14 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         if (e == hipSuccess) e = launch_gemv_down(D, L.hd, out, r, st);
         if (e == hipSuccess) e = mark();
     } else {
-        e = launch_worklist(topk_ids, (int)n, k, E, L.wl, L.hist, st);
+        // experts with few pairs take passes where the shapes allow
+        const bool passes = L.max_passes > 0 && sk_supported(G, U, D);
+        Worklist wl = L.wl;
+        if (!passes) {
+            wl.spass = nullptr;
+            wl.n_spass = nullptr;
+        }
+        e = launch_worklist(topk_ids, (int)n, k, E, wl, L.hist, st);
         if (e == hipSuccess)
             e = launch_xprep(static_cast<const uint16_t *>(x), tokens, H, L.x16, L.xinv, st);
         if (e == hipSuccess) e = mark();
@@ -700,9 +735,17 @@ int qmoe_layer_ex(const qmoe_layer_desc *desc, int32_t x_dtype, const void *x, i
         r.max_tiles = L.max_tiles;
         r.x_rows = tokens;
         r.h_rows = n;
+        SkRoute sr{};
+        sr.wl = L.wl;
+        sr.topk_w = topk_w;
+        sr.k = k;
+        sr.max_passes = L.max_passes;
         if (e == hipSuccess) e = launch_mfma_gateup(G, U, L.x16, L.xinv, L.h16, r, st);
+        if (e == hipSuccess && passes)
+            e = launch_sk_gateup(G, U, L.x16, tokens, L.xinv, L.h16, sr, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_mfma_down(D, L.h16, nullptr, L.y, r, st);
+        if (e == hipSuccess && passes) e = launch_sk_down(D, L.h16, n, L.y, sr, st);
         if (e == hipSuccess) e = mark();
         if (e == hipSuccess) e = launch_combine(L.y, L.wl.inv, tokens, k, H, out, st);
         if (e == hipSuccess) e = mark();

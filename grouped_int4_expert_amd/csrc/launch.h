@@ -43,6 +43,11 @@ struct Worklist {
     int32_t *tiles;     // [2*max_tiles] (expert, first row)   (nullable)
     int32_t *n_tiles;   // [1]                                 (nullable)
     int tile_m;         // rows per tile
+    // Prefill passes (with tiles only): experts with 1..skinny_max pairs are
+    // cut into SK_TP-row passes (expert, first row) instead of tiles.
+    int32_t *spass;     // [2*max_passes]                      (nullable)
+    int32_t *n_spass;   // [1]                                 (nullable)
+    int skinny_max;
 };
 
 // Decode activation digits of `rows` rows of width `cols` (see common.h).
@@ -228,6 +233,25 @@ hipError_t launch_mfma_down(const QMat &down, const uint16_t *h16, float *out, Y
 // out[t] = sum_j Y[inv[t*k + j]] in pick order (dropped pairs skipped).
 hipError_t launch_combine(YBuf y, const int32_t *inv, int tokens, int k, int hidden, float *out,
                           hipStream_t st);
+
+// Prefill passes of lightly routed experts (skinny.hip): SK_TP rows each,
+// weights streamed once per pass on the matrix cores; the same h16 and Y as
+// the tile kernels.
+constexpr int SK_TP = 16;
+// Experts with at most this many pairs take passes by default.
+constexpr int PREFILL_PASS_ROWS_DEFAULT = 16;
+struct SkRoute {
+    Worklist wl;           // counts, offsets, pairs, spass, n_spass
+    const float *topk_w;
+    int k;
+    int max_passes;        // bound on n_spass
+};
+bool sk_supported(const QMat &gate, const QMat &up, const QMat &down);
+hipError_t launch_sk_gateup(const QMat &gate, const QMat &up, const uint16_t *x16, int tokens,
+                            const float *xinv, uint16_t *h16, const SkRoute &r, hipStream_t st);
+hipError_t launch_sk_down(const QMat &down, const uint16_t *h16, int64_t pairs, YBuf y,
+                          const SkRoute &r, hipStream_t st);
+
 
 // Router: ids [tokens][k] (pick order) and softmax weights over the picked
 // logits, one wave per token.

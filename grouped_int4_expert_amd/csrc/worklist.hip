@@ -12,7 +12,8 @@
 // The same pass also lists the experts that have work (ascending) and cuts
 // each expert's rows into tiles of tile_m rows for the grouped GEMMs: at
 // most ceil(n / tile_m) + E tiles, so grids are launched at that bound and
-// surplus blocks exit.
+// surplus blocks exit.  For the bf16 prefill, experts with at most
+// skinny_max pairs are listed as 16-pair passes instead (skinny.hip).
 #include "common.h"
 #include "launch.h"
 #include "split16.h"
@@ -134,7 +135,9 @@ __device__ void wl_block(const int32_t *__restrict__ ids, int n, int E, const Wo
         if (tid == 0) wl.n_active[0] = na;
     }
     if (b == 0 && wl.tiles) {
-        const int nt = (my + wl.tile_m - 1) / wl.tile_m;
+        // experts with 1..skinny_max pairs take SK_TP-row passes instead
+        const bool pass = wl.spass && my <= wl.skinny_max;
+        const int nt = pass ? 0 : (my + wl.tile_m - 1) / wl.tile_m;
         int ntot;
         const int t0 = block_exclusive_scan(nt, sh.wave, &ntot);
         for (int i = 0; i < nt; i++) {
@@ -142,6 +145,16 @@ __device__ void wl_block(const int32_t *__restrict__ ids, int n, int E, const Wo
             wl.tiles[2 * (t0 + i) + 1] = i * wl.tile_m;
         }
         if (tid == 0) wl.n_tiles[0] = ntot;
+        if (wl.spass) {
+            const int np = pass ? (my + SK_TP - 1) / SK_TP : 0;
+            int ptot;
+            const int p0 = block_exclusive_scan(np, sh.wave, &ptot);
+            for (int i = 0; i < np; i++) {
+                wl.spass[2 * (p0 + i)] = tid;
+                wl.spass[2 * (p0 + i) + 1] = i * SK_TP;
+            }
+            if (tid == 0) wl.n_spass[0] = ptot;
+        }
     }
 
     // 4. stable fill: pairs of this block in order, one wave at a time

@@ -101,7 +101,14 @@ enum {
  *    become f16 subnormals and lose relative precision, below about 2^-16
  *    the rounding alone approaches the 2e-3 bar), and the gated
  *    intermediate h is stored as f16 (|h| < 65504, larger values giving
- *    inf); the accumulators and every output are f32.
+ *    inf); the accumulators and every output are f32.  Experts that receive
+ *    at most qmoe_prefill_pass_rows() pairs (skewed routing leaves many
+ *    such experts) run as weight-streaming passes of up to 16 pairs when
+ *    hidden and inter are multiples of 512 up to 6144 and groups hold 64 or
+ *    more inputs: the codes are exact f16 values, x16 (bf16 scaled by a
+ *    power of two per token, exact in f16) and h are the other operand, and
+ *    each 64-input group's f32 sums are multiplied by the f32 scale, so q * s
+ *    is not rounded there; h is f16 as on the tile path.
  * A NaN or infinity in x reaches every output it feeds on the f32 and bf16
  * paths. */
 enum { QMOE_F32 = 0, QMOE_BF16 = 1, QMOE_F32_DIGITS = 2 };
@@ -327,6 +334,13 @@ int qmoe_cache_prepare_device(qmoe_expert_cache *cache, void *dev_state, size_t 
  * (QMOE_ERR_ALIAS).  tokens == 0 launches nothing. */
 int qmoe_route(const float *logits, int32_t tokens, int32_t experts, int32_t k,
                int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Largest number of pairs an expert may receive in a bf16 layer call and
+ * still take the weight-streaming passes instead of row tiles (see
+ * QMOE_BF16; 0: every expert takes tiles).  Read once per process: the
+ * default, or the environment variable QMOE_PREFILL_PASS_ROWS (0 .. 256).
+ * The bf16 workspace size depends on it. */
+int32_t qmoe_prefill_pass_rows(void);
 
 /* Workspace bytes qmoe_layer needs for these sizes and dtype. */
 size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,

@@ -86,18 +86,21 @@ def check(got, ref, mag=None, path="f32", what=""):
     return err, worst
 
 
-def cover_tokens(ids, E, tile=256, extra=()):
+def cover_tokens(ids, E, tile=256, extra=(), pass_rows=0, pass_tile=16):
     """Tokens whose rows touch every tile of every expert's rows in the
-    worklist (the stable sort of pairs by expert, cut into `tile`-row tiles):
-    a greedy set cover, plus the given extra tokens.  ids int32 [T, k]."""
+    worklist (the stable sort of pairs by expert, cut into `tile`-row tiles,
+    or into `pass_tile`-row passes for experts with at most `pass_rows`
+    pairs): a greedy set cover, plus the given extra tokens.  ids int32
+    [T, k]."""
     ids = np.asarray(ids)
     T, k = ids.shape
     wl = orc().worklist(ids.astype(np.int32), E)
     tiles = []
     for e in range(E):
         off, c = int(wl["offsets"][e]), int(wl["counts"][e])
-        for i in range(0, c, tile):
-            pos = wl["pairs"][off + i: off + min(i + tile, c)]
+        step = pass_tile if c <= pass_rows else tile
+        for i in range(0, c, step):
+            pos = wl["pairs"][off + i: off + min(i + step, c)]
             tiles.append(set(int(p) // k for p in pos))
     chosen = set(int(t) for t in extra)
     left = [tl for tl in tiles if not (tl & chosen)]
@@ -110,6 +113,14 @@ def cover_tokens(ids, E, tile=256, extra=()):
         chosen.add(best)
         left = [tl for tl in left if best not in tl]
     return sorted(chosen)
+
+
+def pass_rows_for(L, dtype):
+    """qmoe_prefill_pass_rows() where layer L's bf16 call takes passes (hidden
+    and inter multiples of 512 up to 6144, groups of 64 or more), else 0."""
+    ok = (dtype == "bf16" and L.H % 512 == 0 and L.F % 512 == 0 and L.H <= 6144
+          and L.F <= 6144 and L.group >= 64)
+    return qm.qmoe_prefill_pass_rows() if ok else 0
 
 
 _ORC = None

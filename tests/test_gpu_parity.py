@@ -11,7 +11,8 @@ import torch
 
 import grouped_int4_expert_amd as qm
 import synth
-from gpu_util import BF16_TOL, F32_TOL, Layer, check, cover_tokens, orc, rel_l2, say
+from gpu_util import (BF16_TOL, F32_TOL, Layer, check, cover_tokens, orc, pass_rows_for,
+                      rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,7 +168,8 @@ def _layer_case(L, T, k, dtype, logits="normal", seed=0, tokens=None, mutate=Non
         ids, w = mutate(ids, w)
     out = qm.qmoe_layer(L.dev, x.to(DEV), ids.to(DEV), w.to(DEV)).cpu().numpy()
     if cover:
-        tokens = cover_tokens(ids.numpy(), L.E, 256, extra=tokens or ())
+        tokens = cover_tokens(ids.numpy(), L.E, 256, extra=tokens or (),
+                              pass_rows=pass_rows_for(L, dtype))
         say(f"  {len(tokens)} tokens cover every worklist tile")
     ref, mag = L.oracle_layer(x, ids, w, tokens, mag=True)
     if tokens is not None:
