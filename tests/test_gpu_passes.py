@@ -165,3 +165,45 @@ def test_passes_worklist_lists_passes():
     ref = orc().worklist(ids.numpy(), 16)
     for key in ("counts", "offsets", "pairs", "inv"):
         assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+
+
+def test_passes_max_experts_invalid_and_duplicate_ids():
+    # E = 1024 (most experts get one pair or none), ids outside [0, E) in some
+    # slots (dropped) and a repeated expert inside some tokens.
+    say("bf16 passes E=1024 H=512 F=512 T=60 k=8, invalid and duplicate ids")
+    L = Layer(1024, 512, 512, seed=79)
+    x, ids, w = _inputs(L, 60, 8, 79)
+    ids = ids.clone()
+    ids[3, 2] = -1
+    ids[7, 0] = 1024
+    ids[11, 5] = 99999
+    ids[20, 1] = ids[20, 0]
+    ids[21, 4] = ids[21, 3]
+    out = _run(L, x, ids, w)
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "bf16", "layer")
+
+
+def test_passes_graph_replays_match_eager():
+    # The pass kernels under HIP graph capture (hidden 6144: the gate+up
+    # passes use more than 64 KB of LDS): every replay (with a stale
+    # workspace and eager work in between) gives the eager result bit for bit.
+    say("bf16 passes: graph replays")
+    L = Layer(4, 6144, 512, seed=80)
+    x, ids, w = _inputs(L, 33, 2, 80)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), w.to(DEV)
+    ws = torch.empty(L.dev.workspace_bytes(33, 2, qm.QMOE_BF16), dtype=torch.uint8, device=DEV)
+    out = torch.empty(33, 6144, device=DEV)
+    qm.qmoe_layer(L.dev, xd, idd, wd, out=out, ws=ws)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+        qm.qmoe_layer(L.dev, xd, idd, wd, out=out, ws=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
