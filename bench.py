@@ -458,26 +458,34 @@ def time_layer_e256(qm, synth, torch, dev, calls=16, reps=3):
 
 
 def stream_probe(torch, dev, reps=5):
-    """Plain device streams at the decode working-set sizes: a read (sum of
-    an f32 buffer) and a copy, each over a set of buffers whose total exceeds
-    the Infinity Cache, so every pass reads from HBM.  GB/s per size (the
-    read counts the bytes read, the copy bytes read + written)."""
+    """Plain device streams at the decode working-set sizes, each over a set
+    of buffers whose total exceeds the Infinity Cache, so every pass reads
+    from HBM: torch's read (sum of an f32 buffer) and copy, and the library's
+    read probe with its two load shapes (1 KB per wave instruction; 16 rows x
+    256 B per row block, the matrix-core decode weight stream).  GB/s per size
+    (reads count the bytes read, the copy bytes read + written)."""
+    import grouped_int4_expert_amd as qm
+    qm.load()
     res = {}
+    sink = torch.empty(qm.QMOE_PROBE_SINK, dtype=torch.int32, device=dev)
     for mb in (56, 85, 290, 1024):
         n = mb * (1 << 20) // 4
         nbuf = max(2, -(-2048 // mb))
         bufs = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(nbuf)]
         dst = torch.empty(n, dtype=torch.float32, device=dev)
         acc = torch.empty(nbuf, dtype=torch.float32, device=dev)
-        for name in ("read", "copy"):
+        for name in ("read", "copy", "probe_linear", "probe_rows"):
             def run():
                 for i, b in enumerate(bufs):
                     if name == "read":
                         torch.sum(b, dim=0, out=acc[i])
-                    else:
+                    elif name == "copy":
                         dst.copy_(b)
+                    else:
+                        qm.qmoe_stream_probe(b, qm.QMOE_PROBE_LINEAR if name == "probe_linear"
+                                             else qm.QMOE_PROBE_ROWS, sink=sink)
             best = time_graph(torch, run, reps)
-            moved = nbuf * n * 4 * (1 if name == "read" else 2)
+            moved = nbuf * n * 4 * (2 if name == "copy" else 1)
             res[f"{name}_{mb}MB"] = round(moved / (best * 1e-3) / 1e9, 1)
         del bufs, dst, acc
         torch.cuda.empty_cache()
@@ -703,8 +711,9 @@ def main():
                     help="run a plain 1 GiB device copy three times and exit "
                          "(reference for HBM byte counters)")
     ap.add_argument("--stream-probe", action="store_true",
-                    help="time plain device reads and copies at 56 MB, 85 MB, 290 MB and "
-                         "1 GB (the HBM rates the decode fractions sit beside) and exit")
+                    help="time plain device reads and copies and the library's read probe at "
+                         "56 MB, 85 MB, 290 MB and 1 GB (the HBM rates the decode fractions "
+                         "sit beside) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -64,7 +64,8 @@ EXPORTS = ["qmoe_abi_version", "qmoe_status_str", "qmoe_packed_bytes", "qmoe_sca
            "qmoe_import_twos", "qmoe_detect_group", "qmoe_cache_create", "qmoe_cache_destroy",
            "qmoe_cache_prepare", "qmoe_cache_resident", "qmoe_cache_device_state_bytes",
            "qmoe_cache_device_init", "qmoe_cache_prepare_device", "qmoe_layer_logits_workspace_bytes",
-           "qmoe_layer_logits", "qmoe_layer_noalloc", "qmoe_prefill_pass_rows"]
+           "qmoe_layer_logits", "qmoe_layer_noalloc", "qmoe_prefill_pass_rows",
+           "qmoe_stream_probe"]
 
 _lib = None
 
@@ -120,6 +121,7 @@ def load(path: str | None = None):
         "qmoe_layer_noalloc": (ctypes.c_int, [ctypes.POINTER(qmoe_layer_desc), i32, vp, i32, vp,
                                               vp, i32, vp, vp]),
         "qmoe_prefill_pass_rows": (i32, []),
+        "qmoe_stream_probe": (ctypes.c_int, [vp, i64, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -171,6 +173,20 @@ def _dev(t, name, dtype=None):
 
 def qmoe_abi_version() -> int:
     return int(load().qmoe_abi_version())
+
+
+QMOE_PROBE_LINEAR, QMOE_PROBE_ROWS, QMOE_PROBE_SINK = 0, 1, 2048
+
+
+def qmoe_stream_probe(buf, pattern=QMOE_PROBE_LINEAR, sink=None, stream=None):
+    """Read `buf` (a device tensor) once with the probe's load shape; returns
+    the uint32 sink (per-block dword sums, as int32 storage)."""
+    _dev(buf, "buf")
+    s = sink if sink is not None else torch.empty(QMOE_PROBE_SINK, dtype=torch.int32,
+                                                  device=buf.device)
+    _check(load().qmoe_stream_probe(_ptr(buf), buf.numel() * buf.element_size(), pattern,
+                                    _ptr(s), _stream(stream)), "qmoe_stream_probe")
+    return s
 
 
 def qmoe_prefill_pass_rows() -> int:

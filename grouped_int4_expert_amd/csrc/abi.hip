@@ -485,6 +485,18 @@ int qmoe_import_twos(const uint8_t *twos, int64_t rows, int64_t cols, uint8_t *p
     return status_of(launch_import_twos(twos, rows, cols, packed, as_stream(stream)));
 }
 
+int qmoe_stream_probe(const void *buf, int64_t bytes, int32_t pattern, uint32_t *sink,
+                      void *stream) {
+    if (!buf || !sink) return QMOE_ERR_NULL;
+    if (pattern != QMOE_PROBE_LINEAR && pattern != QMOE_PROBE_ROWS) return QMOE_ERR_UNSUPPORTED;
+    if (bytes <= 0 || bytes > ((int64_t)1 << 30)) return QMOE_ERR_SHAPE;
+    if (pattern == QMOE_PROBE_ROWS && bytes % 2048 != 0) return QMOE_ERR_SHAPE;
+    if (!aligned16(buf) || !aligned4(sink)) return QMOE_ERR_ALIGN;
+    if (probe_grid(pattern) > QMOE_PROBE_SINK) return QMOE_ERR_SHAPE;
+    if (overlap(sink, 4 * (int64_t)QMOE_PROBE_SINK, buf, bytes)) return QMOE_ERR_ALIAS;
+    return status_of(launch_probe(buf, bytes, pattern, sink, as_stream(stream)));
+}
+
 int32_t qmoe_detect_group(int64_t rows, int64_t cols, int64_t scale_bytes) {
     static const int64_t cand[8] = {16, 32, 48, 64, 96, 128, 192, 256};
     if (rows <= 0 || cols <= 0 || scale_bytes <= 0) return 0;

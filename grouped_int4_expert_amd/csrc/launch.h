@@ -253,6 +253,12 @@ hipError_t launch_sk_down(const QMat &down, const uint16_t *h16, int64_t pairs, 
                           const SkRoute &r, hipStream_t st);
 
 
+// Read-stream probe (probe.hip): pattern 0 linear, 1 rows; grid blocks =
+// probe_grid(pattern), one uint32 sum each in sink.
+int probe_grid(int pattern);
+hipError_t launch_probe(const void *buf, int64_t bytes, int pattern, uint32_t *sink,
+                        hipStream_t st);
+
 // Router: ids [tokens][k] (pick order) and softmax weights over the picked
 // logits, one wave per token.
 constexpr int MAX_ROUTE_TOPK = 16;

@@ -342,6 +342,27 @@ int qmoe_route(const float *logits, int32_t tokens, int32_t experts, int32_t k,
  * The bf16 workspace size depends on it. */
 int32_t qmoe_prefill_pass_rows(void);
 
+/* Read-stream probe, a measurement aid beside the path: reads `bytes` of
+ * device memory at buf once with one of two load shapes and leaves per-block
+ * sums of the dwords read (mod 2^32) in sink, so timing the call gives the
+ * read rate this GPU reaches with that shape (the decode kernels' practical
+ * ceiling, next to the 8 TB/s specification).
+ *  - QMOE_PROBE_LINEAR: each wave instruction reads 1 KB of consecutive
+ *    bytes, 16 such loads in flight per wave.
+ *  - QMOE_PROBE_ROWS: rows of 2048 bytes (one 4096-input int4 row); a wave
+ *    reads blocks of 16 rows x 256 consecutive bytes per row as four
+ *    back-to-back 16-byte loads per lane, two blocks in flight (the weight
+ *    stream of the matrix-core decode passes); bytes % 2048 == 0.
+ * buf: device, 16-byte aligned, 0 < bytes <= 2^30; sink: device uint32
+ * [QMOE_PROBE_SINK]; the sum of all sink entries equals the sum of the
+ * buffer's dwords mod 2^32.  Errors: QMOE_ERR_NULL, QMOE_ERR_ALIGN,
+ * QMOE_ERR_SHAPE, QMOE_ERR_UNSUPPORTED (other patterns), QMOE_ERR_ALIAS
+ * (sink inside buf). */
+enum { QMOE_PROBE_LINEAR = 0, QMOE_PROBE_ROWS = 1 };
+#define QMOE_PROBE_SINK 2048
+int qmoe_stream_probe(const void *buf, int64_t bytes, int32_t pattern, uint32_t *sink,
+                      void *stream);
+
 /* Workspace bytes qmoe_layer needs for these sizes and dtype. */
 size_t qmoe_layer_workspace_bytes(const qmoe_layer_desc *desc, int32_t tokens,
                                   int32_t k, int32_t x_dtype);

@@ -307,3 +307,17 @@ def test_layer_noalloc_rejections(lib):
     assert need > q.NOALLOC_SCRATCH_BYTES
     assert call(big, dtype=1, T=4096, k=8) == 9
     assert q.qmoe_status_str(9).startswith("needs more workspace")
+
+
+def test_stream_probe_validation(lib):
+    # every case fails before a launch
+    S = FAKE + (4 << 30)   # sink far from the buffer
+    assert lib.qmoe_stream_probe(None, 1024, 0, S, None) == 1   # NULL
+    assert lib.qmoe_stream_probe(FAKE, 1024, 0, None, None) == 1   # NULL
+    assert lib.qmoe_stream_probe(FAKE, 1024, 2, S, None) == 4   # UNSUPPORTED
+    assert lib.qmoe_stream_probe(FAKE, 0, 0, S, None) == 2   # SHAPE
+    assert lib.qmoe_stream_probe(FAKE, (1 << 30) + 16, 0, S, None) == 2   # SHAPE
+    assert lib.qmoe_stream_probe(FAKE, 4096 + 16, 1, S, None) == 2   # SHAPE
+    assert lib.qmoe_stream_probe(FAKE + 8, 1024, 0, S, None) == 3   # ALIGN
+    assert lib.qmoe_stream_probe(FAKE, 1024, 0, S + 2, None) == 3   # ALIGN
+    assert lib.qmoe_stream_probe(FAKE, 1 << 20, 0, FAKE + 4096, None) == 6   # ALIAS
