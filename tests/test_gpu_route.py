@@ -71,12 +71,14 @@ def test_route_feeds_layer():
     assert err <= F32_TOL
 
 
-@pytest.mark.parametrize("dtype,T", [("f32", 9), ("bf16", 300)])
-def test_layer_logits_matches_route_then_layer(dtype, T):
-    say(f"layer from logits E=16 H=256 F=128 T={T} k=4 {dtype}")
-    L = Layer(16, 256, 128, seed=27)
+# (512, 512, bf16, 40 tokens: every expert takes the prefill passes)
+@pytest.mark.parametrize("dtype,T,H,F", [("f32", 9, 256, 128), ("bf16", 300, 256, 128),
+                                         ("bf16", 40, 512, 512)])
+def test_layer_logits_matches_route_then_layer(dtype, T, H, F):
+    say(f"layer from logits E=16 H={H} F={F} T={T} k=4 {dtype}")
+    L = Layer(16, H, F, seed=27)
     g = synth.generator(28)
-    x = synth.rand_x(g, (T, 256))
+    x = synth.rand_x(g, (T, H))
     if dtype == "bf16":
         x = synth.to_bf16_rne(x)
     logits = synth.normal_logits(g, T, 16)
