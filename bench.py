@@ -450,6 +450,35 @@ def time_layer_e256(qm, synth, torch, dev, calls=16, reps=3):
         "alg_bytes": pb, "alg_flops": pf, "pass_rows": qm.qmoe_prefill_pass_rows(),
         "phase_ms": {"worklist": round(ph[0], 4), "gate_up": round(ph[1], 4),
                      "down": round(ph[2], 4), "combine": round(ph[3], 4)}}
+    # One GPU's share under 8-way expert parallelism (design only, no second
+    # GPU is used): shard s holds experts 32 s .. 32 s + 31 and runs the same
+    # prefill kernels on the pairs routed to them (other ids dropped); the
+    # slowest shard bounds an expert-parallel step (exchanges not included).
+    shard_ms, shard_pairs = [], []
+    for sh in range(8):
+        sl = slice(32 * sh, 32 * sh + 32)
+        lay_s = qm.QLayer(pk["qg"][sl], w["sg"][sl], pk["qu"][sl], w["su"][sl], pk["qd"][sl],
+                          w["sd"][sl], H2, F2)
+        ids_s = torch.where((ip >= 32 * sh) & (ip < 32 * sh + 32), ip - 32 * sh,
+                            torch.full_like(ip, -1))
+        ws_s = torch.empty(lay_s.workspace_bytes(2048, K, qm.QMOE_BF16), dtype=torch.uint8,
+                           device=dev)
+        qm.qmoe_layer_ex(lay_s, xp, ids_s, wp, evs, out=op, ws=ws_s)
+        b_s = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            qm.qmoe_layer_ex(lay_s, xp, ids_s, wp, evs, out=op, ws=ws_s)
+            torch.cuda.synchronize()
+            ms = evs[0].elapsed_time(evs[4])
+            b_s = ms if b_s is None else min(b_s, ms)
+        shard_ms.append(round(b_s, 4))
+        shard_pairs.append(int((ids_s >= 0).sum()))
+        del lay_s, ws_s
+    res["prefill_t2048_ep8_shards"] = {
+        "ms": shard_ms, "pairs": shard_pairs, "slowest_ms": max(shard_ms),
+        "one_gpu_ms": round(best, 4),
+        "note": "per-GPU prefill kernels of an 8-way expert-parallel split (experts 32s..32s+31 "
+                "per shard; the all-to-all exchanges are not included)"}
     res["config"] = {"workload": "layer_e256_h6144_f2048_top8_zipf1.1", "experts": E2,
                      "hidden": H2, "inter": F2, "topk": K}
     del layer, pk, w, wsd, wsp
