@@ -200,29 +200,42 @@ constexpr int SK_GU_RB = 8;    // 4 x 16 features of gate and of up per block
 constexpr int SK_DN_RB = 16;   // 256 output features per block
 constexpr int SK_GRID_Y = 64;  // passes in the grid at once (blocks loop over the rest)
 
-bool sk_supported(const QMat &gate, const QMat &up, const QMat &down) {
-    const int H = gate.cols, F = gate.rows;
-    return gate.group >= 64 && up.group >= 64 && down.group >= 64 && H % MFD_KW == 0 &&
-           H <= MFD_KW * MFD_GU_WAVES && F % MFD_KW == 0 && F <= MFD_DOWN_MAX_COLS &&
-           H % 16 == 0;
-}
-
 static size_t sk_lds(int cols, int rb) {
     const int S = cols / MFD_KW;
     return (size_t)S * (rb * 4 + MFD_STAGES * 2) * QMOE_WAVE * sizeof(float);
 }
 
+// LDS of one gfx950 workgroup
+constexpr size_t SK_LDS_MAX = 160 * 1024;
+
+// hidden and inter multiples of 512 (one wave per 512 inputs), groups of 64
+// or more, and blocks whose partials fit the LDS: gate+up up to hidden 6144
+// (108 KB), down up to inter 4608 (153 KB)
+bool sk_supported(const QMat &gate, const QMat &up, const QMat &down) {
+    const int H = gate.cols, F = gate.rows;
+    return gate.group >= 64 && up.group >= 64 && down.group >= 64 && H % MFD_KW == 0 &&
+           H <= MFD_KW * MFD_GU_WAVES && F % MFD_KW == 0 && F <= MFD_DOWN_MAX_COLS &&
+           sk_lds(H, SK_GU_RB) <= SK_LDS_MAX && sk_lds(F, SK_DN_RB) <= SK_LDS_MAX;
+}
+
 // gfx950 gives a block up to 160 KB of LDS; above 64 KB the launch needs the
-// kernel's dynamic limit raised (once per kernel, to the largest size used).
+// kernel's dynamic limit raised (once per kernel and device, to the largest
+// size used there).
+constexpr int SK_MAX_DEVICES = 64;
 template <typename K>
-static hipError_t sk_allow_lds(K kernel, size_t lds, std::atomic<size_t> &raised) {
-    if (lds <= 65536 || lds <= raised.load()) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess) raised.store(lds);
+static hipError_t sk_allow_lds(K kernel, size_t lds, std::atomic<size_t> (&raised)[SK_MAX_DEVICES]) {
+    if (lds <= 65536) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::atomic<size_t> *r = dev >= 0 && dev < SK_MAX_DEVICES ? &raised[dev] : nullptr;
+    if (r && lds <= r->load()) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess && r) r->store(lds);
     return e;
 }
-static std::atomic<size_t> sk_gu_lds{0}, sk_dn_lds{0};
+static std::atomic<size_t> sk_gu_lds[SK_MAX_DEVICES], sk_dn_lds[SK_MAX_DEVICES];
 
 hipError_t launch_sk_gateup(const QMat &gate, const QMat &up, const uint16_t *x16, int tokens,
                             const float *xinv, uint16_t *h16, const SkRoute &r, hipStream_t st) {

@@ -104,8 +104,8 @@ enum {
  *    inf); the accumulators and every output are f32.  Experts that receive
  *    at most qmoe_prefill_pass_rows() pairs (skewed routing leaves many
  *    such experts) run as weight-streaming passes of up to 16 pairs when
- *    hidden and inter are multiples of 512 up to 6144 and groups hold 64 or
- *    more inputs: the codes are exact f16 values, x16 (bf16 scaled by a
+ *    hidden and inter are multiples of 512 (hidden up to 6144, inter up to
+ *    4608) and groups hold 64 or more inputs: the codes are exact f16 values, x16 (bf16 scaled by a
  *    power of two per token, exact in f16) and h are the other operand, and
  *    each 64-input group's f32 sums are multiplied by the f32 scale, so q * s
  *    is not rounded there; h is f16 as on the tile path.

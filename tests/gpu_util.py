@@ -117,9 +117,10 @@ def cover_tokens(ids, E, tile=256, extra=(), pass_rows=0, pass_tile=16):
 
 def pass_rows_for(L, dtype):
     """qmoe_prefill_pass_rows() where layer L's bf16 call takes passes (hidden
-    and inter multiples of 512 up to 6144, groups of 64 or more), else 0."""
+    and inter multiples of 512, hidden up to 6144, inter up to 4608, groups of
+    64 or more), else 0."""
     ok = (dtype == "bf16" and L.H % 512 == 0 and L.F % 512 == 0 and L.H <= 6144
-          and L.F <= 6144 and L.group >= 64)
+          and L.F <= 4608 and L.group >= 64)
     return qm.qmoe_prefill_pass_rows() if ok else 0
 
 

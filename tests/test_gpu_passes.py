@@ -207,3 +207,15 @@ def test_passes_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), rep
+
+
+@pytest.mark.parametrize("F", [4608, 6144])
+def test_passes_widest_inter(F):
+    # inter 4608 is the widest whose down passes fit the LDS (9 waves, 153 KB);
+    # at 6144 every expert takes tiles.  Either way the layer matches.
+    say(f"bf16 E=8 H=512 F={F} T=20 k=2 (few pairs per expert)")
+    L = Layer(8, 512, F, seed=81)
+    x, ids, w = _inputs(L, 20, 2, 81)
+    out = _run(L, x, ids, w)
+    ref, mag = L.oracle_layer(x, ids, w, mag=True)
+    check(out, ref, mag, "bf16", "layer")
