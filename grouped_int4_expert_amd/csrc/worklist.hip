@@ -97,11 +97,19 @@ __device__ void wl_block(const int32_t *__restrict__ ids, int n, int E, const Wo
         }
     } else {
         for (int e = tid; e <= E; e += blockDim.x) {
+            // eight independent loads in flight at a time (a plain loop
+            // waits for each block's count before loading the next)
             int tot = 0, pre = 0;
-            for (int j = 0; j < nb; j++) {
-                const int c = hist[(int64_t)j * (E + 1) + e];
-                tot += c;
-                pre += (j < b) ? c : 0;
+            for (int j0 = 0; j0 < nb; j0 += 8) {
+                int c[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++)
+                    c[u] = j0 + u < nb ? hist[(int64_t)(j0 + u) * (E + 1) + e] : 0;
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    tot += c[u];
+                    pre += (j0 + u < b) ? c[u] : 0;
+                }
             }
             sh.tot[e] = tot;
             sh.run[e] = pre;
