@@ -86,26 +86,29 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t *__restrict__
     }
 }
 
-// out[t][n..n+3] = sum over j in pick order of Y[inv[t k + j]][n..n+3]; the
-// four columns share one exponent (n % 4 == 0 stays inside a 16-column block).
-// Token t = blockIdx.z * gridDim.y + blockIdx.y (a grid dimension other than
-// x holds at most 65535 blocks).
+// out[t][n..n+7] = sum over j in pick order of Y[inv[t k + j]][n..n+7]; the
+// eight columns share one exponent (n % 8 == 0 stays inside a 16-column
+// block), one 16-byte load per row.  Token t = blockIdx.z * gridDim.y +
+// blockIdx.y (a grid dimension other than x holds at most 65535 blocks).
 __global__ void __launch_bounds__(256) combine_kernel(YBuf y, const int32_t *__restrict__ inv,
                                                       int tokens, int k, int hidden,
                                                       float *__restrict__ out) {
     const int t = blockIdx.z * gridDim.y + blockIdx.y;
-    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 8;
     if (t >= tokens || n >= hidden) return;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; j++) {
         const int pos = inv[(int64_t)t * k + j];
         if (pos >= 0) {
-            const f16x4 v = *(const f16x4 *)(y.v + (int64_t)pos * hidden + n);
+            const f16x8 v = *(const f16x8 *)(y.v + (int64_t)pos * hidden + n);
             const float sc = ldexpf(1.0f, (int)y.e[(int64_t)pos * (hidden / 16) + n / 16] - 15);
-            acc += f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]} * sc;
+            lo += f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]} * sc;
+            hi += f32x4{(float)v[4], (float)v[5], (float)v[6], (float)v[7]} * sc;
         }
     }
-    *(f32x4 *)(out + (int64_t)t * hidden + n) = acc;
+    float *o = out + (int64_t)t * hidden + n;
+    *(f32x4 *)o = lo;
+    *(f32x4 *)(o + 4) = hi;
 }
 
 hipError_t launch_xprep(const uint16_t *x, int tokens, int hidden, uint16_t *x16, float *xinv,
@@ -124,7 +127,7 @@ hipError_t launch_mfma_gateup(const QMat &gate, const QMat &up, const uint16_t *
 hipError_t launch_combine(YBuf y, const int32_t *inv, int tokens, int k, int hidden, float *out,
                           hipStream_t st) {
     const int gy = tokens < 65535 ? tokens : 65535;
-    const dim3 grid((hidden / 4 + 255) / 256, gy, (tokens + gy - 1) / gy);
+    const dim3 grid((hidden / 8 + 255) / 256, gy, (tokens + gy - 1) / gy);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, y, inv, tokens, k, hidden, out);
     return hipGetLastError();
 }
