@@ -521,6 +521,29 @@ def stream_probe(torch, dev, reps=5):
     return res
 
 
+def vendor_gemm(torch, dev, reps=5):
+    """The vendor's dense f16 GEMM (torch.matmul on contiguous 2-D operands,
+    hipBLASLt underneath) at the shapes of the 8192-token prefill layer with
+    every pair's rows stacked: gate+up 65536 x 4096 by 4096 x 3072 and down
+    65536 x 1536 by 1536 x 4096.  Best of `reps` graph replays; a reference
+    beside the MFMA kernels, which also unpack int4 and gather rows."""
+    res = {}
+    rows = 8 * 8192
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, k, n in (("gateup", H, 2 * F), ("down", F, H)):
+        a = torch.randn(rows, k, generator=g, device=dev).to(torch.float16)
+        b = torch.randn(k, n, generator=g, device=dev).to(torch.float16)
+        c = torch.empty(rows, n, dtype=torch.float16, device=dev)
+        best = time_graph(torch, lambda: torch.matmul(a, b, out=c), reps)
+        flops = 2.0 * rows * k * n
+        res[name] = {"m": rows, "k": k, "n": n, "ms": round(best, 4),
+                     "TFLOPs": round(flops / (best * 1e-3) / 1e12, 1),
+                     "frac_of_peak": round(flops / (best * 1e-3) / BF16_PEAK, 4)}
+        del a, b, c
+        torch.cuda.empty_cache()
+    return res
+
+
 def expert_bytes(group):
     """Packed codes + f32 scales of one expert (gate, up, down) for a group size."""
     return 2 * (F * H // 2 + F * (-(-H // group)) * 4) + (H * F // 2 + H * (-(-F // group)) * 4)
@@ -739,6 +762,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy three times and exit "
                          "(reference for HBM byte counters)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the vendor dense f16 GEMM (torch.matmul) at the prefill "
+                         "layer's two shapes and exit (a reference beside the MFMA kernels)")
     ap.add_argument("--stream-probe", action="store_true",
                     help="time plain device reads and copies and the library's read probe at "
                          "56 MB, 85 MB, 290 MB and 1 GB (the HBM rates the decode fractions "
@@ -767,6 +793,9 @@ def main():
         return
     if args.stream_probe:
         print(json.dumps({"stream_probe_GBps": stream_probe(torch, dev)}), flush=True)
+        return
+    if args.vendor_gemm:
+        print(json.dumps({"vendor_gemm": vendor_gemm(torch, dev)}), flush=True)
         return
 
     # ---------------- inputs, resident in HBM before timing ----------------
